@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs for the Grok-1 attention sub-layer core.
+
+This module only draws numbers: it holds none of the method's arithmetic
+(no RoPE, no norm, no attention, no projection). Both the fp64 oracle's tests
+and the GPU path's tests and benchmark take their inputs from here, so the two
+sides see exactly the same values.
+
+Conventions
+-----------
+* Generator: ``numpy.random.Generator(PCG64(seed))``.
+* Real-valued tensors are drawn as float32 ``standard_normal`` samples. A
+  bf16 tensor is that float32 sample rounded to the nearest bf16
+  (round-half-to-even) and is handed out as its raw ``uint16`` bit pattern.
+* int8 weights are uniform integers in [-127, 127].
+* Sequence lengths of the ragged decode workload are uniform integers in
+  [512, 8192] (both ends included).
+
+The five workloads mirror the shapes the pages describe for Grok-1
+(48 query heads, 8 KV heads, head size 128, context 8192, model width 6144):
+see ``WORKLOADS``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "f32_to_bf16_bits",
+    "Workload",
+    "WORKLOADS",
+    "rng",
+    "normal_f32",
+    "normal_bf16",
+    "int8_uniform",
+    "make_prefill_inputs",
+    "make_decode_inputs",
+    "make_sublayer_inputs",
+    "make_workload",
+]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); return uint16 bits.
+
+    Encoding of drawn samples only; NaN is not expected from a normal draw.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def normal_f32(g: np.random.Generator, shape) -> np.ndarray:
+    return g.standard_normal(size=shape, dtype=np.float32)
+
+
+def normal_bf16(g: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """bf16 bits of N(0,1) float32 draws; drawn in chunks to bound host memory."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = f32_to_bf16_bits(g.standard_normal(size=e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def int8_uniform(g: np.random.Generator, shape) -> np.ndarray:
+    return g.integers(-127, 128, size=shape, dtype=np.int8)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "prefill" | "decode" | "sublayer"
+    seed: int
+    dtype: str  # "f32" | "bf16"
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    T: int = 1  # query tokens per sequence
+    Tmax: int = 0  # KV-cache capacity (decode)
+    d_model: int = 0  # sub-layer width
+    logit_scale_factor: float = 1.0  # multiplies 1/sqrt(D)
+    softcap: float = 30.0
+    rope_base: float = 10000.0
+    eps: float = 1e-5
+    ragged: bool = False
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def attn_mult(self) -> float:
+        """Logit multiplier, returned as the float32 value passed to kernels."""
+        return float(np.float32(self.logit_scale_factor / math.sqrt(self.D)))
+
+
+WORKLOADS = {
+    # Tiny fp32 causal prefill: one KV head shared by six query heads.
+    "c1_tiny_prefill_f32": Workload(
+        name="c1_tiny_prefill_f32", kind="prefill", seed=1001, dtype="f32",
+        B=1, T=16, Hq=6, Hkv=1, D=32),
+    # Single-token decode against a full 8192-slot cache.
+    "c2_decode_b1": Workload(
+        name="c2_decode_b1", kind="decode", seed=1002, dtype="bf16",
+        B=1, Hq=48, Hkv=8, D=128, Tmax=8192),
+    # 8k causal prefill with the logit multiplier raised 4x.
+    "c3_prefill_t8192": Workload(
+        name="c3_prefill_t8192", kind="prefill", seed=1003, dtype="bf16",
+        B=1, T=8192, Hq=48, Hkv=8, D=128, logit_scale_factor=4.0),
+    # 32 sequences of lengths uniform in [512, 8192], one new token each.
+    "c4_decode_ragged_b32": Workload(
+        name="c4_decode_ragged_b32", kind="decode", seed=1004, dtype="bf16",
+        B=32, Hq=48, Hkv=8, D=128, Tmax=8192, ragged=True),
+    # Full attention sub-layer: norm, int8 projections, RoPE, attention, norm.
+    "c5_sublayer_b4_t2048": Workload(
+        name="c5_sublayer_b4_t2048", kind="sublayer", seed=1005, dtype="bf16",
+        B=4, T=2048, Hq=48, Hkv=8, D=128, d_model=6144),
+}
+
+
+def make_prefill_inputs(B, T, Hq, Hkv, D, seed, dtype="bf16", key_pad_frac=0.0):
+    """q [B,T,Hq,D], k/v [B,T,Hkv,D]; optional key-padding mask [B,T] (1 = keep).
+
+    With ``key_pad_frac > 0`` each key is padding with that probability.
+    """
+    g = rng(seed)
+    draw = normal_f32 if dtype == "f32" else normal_bf16
+    q = draw(g, (B, T, Hq, D))
+    k = draw(g, (B, T, Hkv, D))
+    v = draw(g, (B, T, Hkv, D))
+    key_valid = None
+    if key_pad_frac > 0:
+        key_valid = (g.random((B, T)) >= key_pad_frac).astype(np.uint8)
+    return {"q": q, "k": k, "v": v, "key_valid": key_valid}
+
+
+def make_decode_inputs(B, Hq, Hkv, D, Tmax, seed, lengths=None, ragged=False):
+    """Cache [B,Tmax,Hkv,D] (every slot finite N(0,1), valid or not), new q/k/v
+    [B,1,H,D], and per-sequence step = length-1 (the new token's slot).
+
+    ``lengths[b]`` counts the new token, so the attended keys are
+    slots ``[0, lengths[b])`` after the append.
+    """
+    g = rng(seed)
+    k_cache = normal_bf16(g, (B, Tmax, Hkv, D))
+    v_cache = normal_bf16(g, (B, Tmax, Hkv, D))
+    q = normal_bf16(g, (B, 1, Hq, D))
+    k_new = normal_bf16(g, (B, 1, Hkv, D))
+    v_new = normal_bf16(g, (B, 1, Hkv, D))
+    if lengths is None:
+        if ragged:
+            lengths = g.integers(512, Tmax + 1, size=B)
+        else:
+            lengths = np.full(B, Tmax)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    step = (lengths - 1).astype(np.int32)
+    return {"k_cache": k_cache, "v_cache": v_cache, "q": q, "k_new": k_new,
+            "v_new": v_new, "step": step, "kv_len": lengths.copy()}
+
+
+def make_sublayer_inputs(B, T, d_model, Hq, Hkv, D, seed, scale=0.02 / 127,
+                         distinct_scales=False):
+    """x [B,T,d] bf16; int8 weights Wq [d,Hq*D], Wk/Wv [d,Hkv*D], Wo [Hq*D,d];
+    per-output-channel float32 scales (constant ``scale``, or drawn per channel)."""
+    g = rng(seed)
+    x = normal_bf16(g, (B, T, d_model))
+    wq = int8_uniform(g, (d_model, Hq * D))
+    wk = int8_uniform(g, (d_model, Hkv * D))
+    wv = int8_uniform(g, (d_model, Hkv * D))
+    wo = int8_uniform(g, (Hq * D, d_model))
+
+    def sc(n):
+        if distinct_scales:
+            return (scale * g.uniform(0.5, 1.5, size=n)).astype(np.float32)
+        return np.full(n, scale, dtype=np.float32)
+
+    return {"x": x, "wq": wq, "wk": wk, "wv": wv, "wo": wo,
+            "sq": sc(Hq * D), "sk": sc(Hkv * D), "sv": sc(Hkv * D), "so": sc(d_model)}
+
+
+def make_workload(name: str) -> dict:
+    """All inputs of one named workload at its full size."""
+    w = WORKLOADS[name]
+    if w.kind == "prefill":
+        return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.seed, w.dtype)
+    if w.kind == "decode":
+        return make_decode_inputs(w.B, w.Hq, w.Hkv, w.D, w.Tmax, w.seed, ragged=w.ragged)
+    return make_sublayer_inputs(w.B, w.T, w.d_model, w.Hq, w.Hkv, w.D, w.seed)

@@ -1,0 +1,410 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+None of these re-types the oracle's formula: each check comes from a printed
+example or constant, a closed form, an invariant, or a library routine that a
+special case reduces to (torch's scaled-dot-product attention and rms_norm in
+float64 on the CPU).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import oracle as orc
+from conftest import read_golden_rows
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+# --------------------------------------------------------------------------
+# dtype helpers
+# --------------------------------------------------------------------------
+def test_round_bf16_matches_torch_on_float32_inputs():
+    g = np.random.default_rng(7)
+    x = np.concatenate([
+        g.standard_normal(20000).astype(np.float32) * 10.0 ** g.integers(-6, 6, 20000),
+        # exact ties between two bf16 values: 1 + 2**-8 (tie, even below), 1 + 3*2**-8
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 3.0e38],
+                 dtype=np.float32),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    # and the bit helpers agree with the input generator's encoding
+    np.testing.assert_array_equal(orc.f64_to_bf16_bits(x.astype(np.float64)), gi.f32_to_bf16_bits(x))
+    np.testing.assert_array_equal(orc.bf16_bits_to_f64(gi.f32_to_bf16_bits(x)), ref)
+
+
+# --------------------------------------------------------------------------
+# constants
+# --------------------------------------------------------------------------
+def test_logit_multiplier_is_inverse_sqrt_head_size(golden_constants):
+    m = golden_constants["attn_output_multiplier"]
+    D = int(golden_constants["key_size"])
+    assert np.float32(m) == np.float32(1.0 / math.sqrt(D))
+    assert abs(m - 1.0 / math.sqrt(D)) < 1e-16
+
+
+def test_kv_cache_size_closed_form(golden_constants):
+    c = golden_constants
+    L, T, H, D = int(c["num_layers"]), int(c["max_seq_len"]), int(c["num_kv_heads"]), int(c["key_size"])
+    assert orc.kv_cache_bytes(1, 1, T, H, D) == int(c["kv_bytes_per_layer_per_seq"]) == 32 * 2 ** 20
+    total = orc.kv_cache_bytes(L, 1, T, H, D)
+    assert total == int(c["kv_bytes_64_layers_per_seq"]) == 2 ** 31
+    assert abs(total / 1e9 - 2.15) < 0.01  # the "about 2.15 GB" the pages print
+    assert orc.kv_cache_bytes(L, 1, T, int(c["num_q_heads"]), D) == int(c["mha_kv_bytes_64_layers"])
+    assert orc.kv_cache_bytes(L, 1, T, 1, D) == int(c["mqa_kv_bytes_64_layers"])
+
+
+# --------------------------------------------------------------------------
+# softcap
+# --------------------------------------------------------------------------
+def test_softcap_identity_near_zero_taylor():
+    x = np.linspace(-3, 3, 601)
+    # 30 tanh(x/30) = x - x^3/2700 + 2 x^5/(15*30^4) - ...
+    taylor = x - x ** 3 / 2700.0
+    bound = 2 * np.abs(x) ** 5 / (15 * 30.0 ** 4) * 1.001 + 1e-15
+    assert np.all(np.abs(orc.softcap(x, 30.0) - taylor) <= bound)
+    assert np.all(np.abs(orc.softcap(x[np.abs(x) < 0.1]) - x[np.abs(x) < 0.1]) < 1e-6)
+
+
+def test_softcap_bounded_odd_monotone(golden_constants):
+    cap = golden_constants["softcap"]
+    x = np.linspace(-1e4, 1e4, 200001)
+    y = orc.softcap(x, cap)
+    assert np.all(np.abs(y) <= cap)
+    assert np.all(np.diff(y) >= 0)
+    np.testing.assert_array_equal(orc.softcap(-x, cap), -y)
+    assert orc.softcap(1e4, cap) == pytest.approx(30.0, abs=1e-12)
+    assert orc.softcap(100.0, cap) == pytest.approx(29.92, abs=0.005)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm
+# --------------------------------------------------------------------------
+def test_rmsnorm_constant_vector_closed_form():
+    for c in (0.5, -3.0, 1e-3):
+        x = np.full((2, 6144), c)
+        y = orc.rmsnorm(x, eps=1e-5)
+        np.testing.assert_allclose(y, c / math.sqrt(c * c + 1e-5), rtol=1e-15)
+
+
+def test_rmsnorm_matches_torch_rms_norm_float64():
+    g = np.random.default_rng(3)
+    x = g.standard_normal((5, 96)) * 3
+    gamma = g.uniform(0.5, 2, 96)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(gamma), eps=1e-5)
+    np.testing.assert_allclose(orc.rmsnorm(x, gamma, 1e-5), ref.numpy(), rtol=1e-13, atol=1e-14)
+    # unit gamma gives unit RMS (up to eps)
+    y = orc.rmsnorm(x, None, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
+
+
+def test_rmsnorm_residual_form():
+    x = np.full((1, 8), 2.0)
+    r = np.arange(8.0).reshape(1, 8)
+    y = orc.rmsnorm(x, None, 0.0, residual=r)  # norm(2*1) = 1
+    np.testing.assert_array_equal(y, r + 1.0)
+
+
+# --------------------------------------------------------------------------
+# int8 Linear
+# --------------------------------------------------------------------------
+def test_linear_int8_hand_example_per_output_channel_scale():
+    x = np.array([[1.0, 2.0]])
+    w = np.array([[1, 0, 2], [0, 3, 0]], dtype=np.int8)  # [in=2, out=3]
+    s = np.array([0.5, 2.0, 0.25], dtype=np.float32)  # one scale per output column
+    np.testing.assert_array_equal(orc.linear_int8(x, w, s), [[0.5, 12.0, 0.5]])
+
+
+def test_linear_int8_column_selection():
+    g = np.random.default_rng(5)
+    x = g.standard_normal((4, 3, 16))
+    for k, n in ((0, 0), (7, 3), (15, 5)):
+        w = np.zeros((16, 6), dtype=np.int8)
+        w[k, n] = 127
+        s = np.full(6, 1 / 127, dtype=np.float32)
+        y = orc.linear_int8(x, w, s)
+        assert y.shape == (4, 3, 6)
+        expect = np.zeros_like(y)
+        expect[..., n] = x[..., k] * 127 * np.float64(np.float32(1 / 127))
+        np.testing.assert_allclose(y, expect, rtol=1e-15, atol=0)
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+def test_rope_d4_pairing_worked_example():
+    rows = read_golden_rows("rope_d4_pairing.txt")
+    t = 3
+    inv = orc.rope_inv_freq(4)
+    for a, b, fi in ((int(r[0]), int(r[1]), int(r[2])) for r in rows):
+        x = np.zeros((1, 1, 1, 4))
+        x[..., a] = 1.0
+        y = orc.rope(x, np.array([[t]]))[0, 0, 0]
+        th = np.float64(np.float32(np.float32(t) * inv[fi]))
+        expect = np.zeros(4)
+        expect[a] = math.cos(th)
+        expect[b] = math.sin(th)
+        np.testing.assert_allclose(y, expect, atol=1e-15)
+        # the interleaved layout would have put the sine at a+1 for a even
+        if a + 1 != b:
+            assert abs(y[a + 1]) < 1e-15
+
+
+def test_rope_frequency_spectrum(golden_constants):
+    inv = orc.rope_inv_freq(128, golden_constants["rope_base"])
+    assert inv[0] == 1.0 == golden_constants["rope_w0"]
+    assert inv.dtype == np.float32 and inv.shape == (64,)
+    assert inv[63] == pytest.approx(golden_constants["rope_w63_approx"], rel=0.02)
+    assert np.all(np.diff(inv) < 0)
+
+
+def test_rope_matches_complex_rotation():
+    """x_i + i*x_{i+D/2} multiplied by exp(i*theta_i) (the rotation-matrix form)."""
+    g = np.random.default_rng(11)
+    B, T, H, D = 2, 5, 3, 32
+    x = g.standard_normal((B, T, H, D))
+    pos = np.array([[0, 1, 2, 3, 4], [100, 101, 8191, 4000, 7]])
+    y = orc.rope(x, pos)
+    inv = orc.rope_inv_freq(D)
+    th = (pos.astype(np.float32)[..., None] * inv).astype(np.float32).astype(np.float64)
+    z = (x[..., : D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * th)[:, :, None, :]
+    np.testing.assert_allclose(y[..., : D // 2], z.real, atol=1e-13)
+    np.testing.assert_allclose(y[..., D // 2:], z.imag, atol=1e-13)
+
+
+def test_rope_identity_at_zero_norm_preserving_and_invertible():
+    g = np.random.default_rng(12)
+    x = g.standard_normal((1, 4, 2, 128))
+    np.testing.assert_array_equal(orc.rope(x, np.zeros((1, 4), dtype=int)), x)
+    pos = np.array([[1, 77, 4095, 8191]])
+    y = orc.rope(x, pos)
+    pair = lambda a: a[..., :64] ** 2 + a[..., 64:] ** 2  # noqa: E731
+    np.testing.assert_allclose(pair(y), pair(x), rtol=1e-12)
+    # undo: rotate by -theta, i.e. x = y*cos - rotate_half(y)*sin
+    inv = orc.rope_inv_freq(128)
+    th = (pos.astype(np.float32)[..., None] * inv).astype(np.float32).astype(np.float64)
+    th = np.concatenate((th, th), -1)[:, :, None, :]
+    back = y * np.cos(th) - orc.rotate_half(y) * np.sin(th)
+    np.testing.assert_allclose(back, x, atol=1e-12)
+
+
+def test_rope_dot_depends_only_on_offset():
+    g = np.random.default_rng(13)
+    q = g.standard_normal((1, 1, 1, 128))
+    k = g.standard_normal((1, 1, 1, 128))
+    for m, n, s in ((5, 2, 10), (40, 33, 57), (3, 9, 100)):
+        d1 = np.sum(orc.rope(q, [[m]]) * orc.rope(k, [[n]]))
+        d2 = np.sum(orc.rope(q, [[m + s]]) * orc.rope(k, [[n + s]]))
+        assert d1 == pytest.approx(d2, rel=1e-4, abs=1e-4)
+
+
+# --------------------------------------------------------------------------
+# KV append
+# --------------------------------------------------------------------------
+def test_kv_append_bit_copy_and_untouched_slots():
+    g = np.random.default_rng(21)
+    kc = g.integers(0, 2 ** 16, (3, 16, 2, 8), dtype=np.uint16)
+    vc = g.integers(0, 2 ** 16, (3, 16, 2, 8), dtype=np.uint16)
+    kn = g.integers(0, 2 ** 16, (3, 2, 2, 8), dtype=np.uint16)
+    vn = g.integers(0, 2 ** 16, (3, 2, 2, 8), dtype=np.uint16)
+    step = np.array([0, 5, 14], dtype=np.int32)
+    k2, v2, ns = orc.kv_append(kc, vc, kn, vn, step)
+    np.testing.assert_array_equal(ns, step + 2)
+    for b, s in enumerate(step):
+        np.testing.assert_array_equal(k2[b, s:s + 2], kn[b])
+        np.testing.assert_array_equal(v2[b, s:s + 2], vn[b])
+        keep = np.ones(16, bool)
+        keep[s:s + 2] = False
+        np.testing.assert_array_equal(k2[b, keep], kc[b, keep])
+        np.testing.assert_array_equal(v2[b, keep], vc[b, keep])
+    with pytest.raises(ValueError):
+        orc.kv_append(kc, vc, kn, vn, np.array([0, 0, 15], dtype=np.int32))
+
+
+# --------------------------------------------------------------------------
+# masks
+# --------------------------------------------------------------------------
+def test_causal_mask_matches_printed_6x6():
+    printed = np.array([[int(c) for c in r] for r in read_golden_rows("causal_mask_6x6.txt")], bool)
+    m = orc.attention_mask(np.arange(6)[None, :], 6)[0]
+    np.testing.assert_array_equal(m, printed)
+
+
+def test_decode_mask_is_memory_mask():
+    m = orc.attention_mask(np.array([[9]]), 16, kv_len=np.array([10]))[0, 0]
+    np.testing.assert_array_equal(m, np.arange(16) < 10)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _sdpa64(q, k, v, mask=None, is_causal=False, scale=None, gqa=True):
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    am = None if mask is None else torch.from_numpy(mask)[:, None, :, :]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=am, is_causal=is_causal, scale=scale, enable_gqa=gqa)
+    B, H, T, D = o.shape
+    return o.permute(0, 2, 1, 3).reshape(B, T, H * D).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(6, 1), (12, 2), (8, 8), (48, 8)])
+def test_attention_without_cap_is_textbook_sdpa(Hq, Hkv):
+    """A huge cap makes the softcap the identity: torch SDPA (float64) is then exact."""
+    g = np.random.default_rng(100 + Hq)
+    B, T, D = 2, 13, 16
+    q, k, v = (g.standard_normal((B, T, H, D)) for H in (Hq, Hkv, Hkv))
+    mult = 1 / math.sqrt(D)
+    pos = np.broadcast_to(np.arange(T), (B, T))
+    got = orc.attention(q, k, v, orc.attention_mask(pos, T), mult, cap=1e9)
+    ref = _sdpa64(q, k, v, is_causal=True, scale=mult)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    # with key padding (no fully padded prefix, so every row keeps a valid key)
+    kv = np.ones((B, T), np.uint8)
+    kv[0, [3, 4, 9]] = 0
+    kv[1, [1, 12]] = 0
+    mask = orc.attention_mask(pos, T, key_valid=kv)
+    got = orc.attention(q, k, v, mask, mult, cap=1e9)
+    ref = _sdpa64(q, k, v, mask=mask, scale=mult)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    g = np.random.default_rng(31)
+    B, T, Hq, Hkv, D = 1, 9, 12, 2, 8
+    q = g.standard_normal((B, T, Hq, D))
+    k = g.standard_normal((B, T, Hkv, D)) * 3
+    v = g.standard_normal((B, T, Hkv, D))
+    mask = orc.attention_mask(np.arange(T)[None], T)
+    G = Hq // Hkv
+    krep = np.repeat(k, G, axis=2)  # consecutive repeats: head h uses KV head h // G
+    vrep = np.repeat(v, G, axis=2)
+    a = orc.attention(q, k, v, mask, 0.3, 30.0)
+    b = orc.attention(q, krep, vrep, mask, 0.3, 30.0)
+    np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-15)
+    # the interleaved grouping (h % Hkv) is a different function
+    c = orc.attention(q, np.tile(k, (1, 1, G, 1)), np.tile(v, (1, 1, G, 1)), mask, 0.3, 30.0)
+    assert np.max(np.abs(a - c)) > 1e-3
+
+
+def test_softmax_rows_sum_to_one_and_masked_weights_vanish():
+    g = np.random.default_rng(32)
+    B, T, Hq, Hkv, D = 2, 11, 6, 1, 32
+    q, k, v = (g.standard_normal((B, T, H, D)) * 4 for H in (Hq, Hkv, Hkv))
+    kv = np.ones((B, T), np.uint8)
+    kv[1, 5] = 0
+    mask = orc.attention_mask(np.broadcast_to(np.arange(T), (B, T)), T, key_valid=kv)
+    _, w = orc.attention(q, k, v, mask, 1.0, 30.0, return_weights=True)
+    np.testing.assert_allclose(w.sum(-1), 1.0, rtol=1e-14)
+    assert np.all(w[np.broadcast_to(~mask[:, None, None], w.shape)] == 0.0)
+
+
+def test_logit_multiplier_applies_before_softcap():
+    """Two keys: weights are 1/(1+exp(c1-c0)) with c = cap*tanh(mult*z/cap)."""
+    q = np.zeros((1, 1, 1, 2))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 2, 1, 2))
+    k[0, 0, 0, 0] = 50.0
+    k[0, 1, 0, 0] = 200.0
+    v = np.zeros((1, 2, 1, 2))
+    v[0, 1, 0, 0] = 1.0
+    mask = np.ones((1, 1, 2), bool)
+    mult, cap = 0.5, 30.0
+    o = orc.attention(q, k, v, mask, mult, cap)
+    c0, c1 = cap * math.tanh(25.0 / cap), cap * math.tanh(100.0 / cap)
+    assert o[0, 0, 0] == pytest.approx(1 / (1 + math.exp(c0 - c1)), rel=1e-14)
+    # the other order (cap, then scale) would give a clearly different weight
+    d0, d1 = mult * cap * math.tanh(50 / cap), mult * cap * math.tanh(200 / cap)
+    assert abs(o[0, 0, 0] - 1 / (1 + math.exp(d0 - d1))) > 1e-3
+
+
+def test_causal_row0_is_v0_and_equal_keys_average_visible_values():
+    g = np.random.default_rng(33)
+    B, T, Hq, Hkv, D = 1, 7, 6, 1, 16
+    q = g.standard_normal((B, T, Hq, D))
+    k = g.standard_normal((B, T, Hkv, D))
+    v = g.standard_normal((B, T, Hkv, D))
+    mask = orc.attention_mask(np.arange(T)[None], T)
+    o = orc.attention(q, k, v, mask, 0.25).reshape(B, T, Hq, D)
+    for h in range(Hq):
+        np.testing.assert_array_equal(o[0, 0, h], v[0, 0, 0])
+    k_eq = np.broadcast_to(k[:, :1], k.shape)
+    o = orc.attention(q, k_eq, v, mask, 0.25).reshape(B, T, Hq, D)
+    for t in range(T):
+        np.testing.assert_allclose(o[0, t, 2], v[0, : t + 1, 0].mean(0), rtol=1e-13, atol=1e-15)
+
+
+def test_fully_masked_row_is_uniform_over_all_keys():
+    g = np.random.default_rng(34)
+    B, T, Hq, Hkv, D = 1, 6, 2, 1, 4
+    q, k, v = (g.standard_normal((B, T, H, D)) for H in (Hq, Hkv, Hkv))
+    kv = np.array([[0, 0, 1, 1, 1, 1]], np.uint8)  # rows 0 and 1 see no valid key
+    mask = orc.attention_mask(np.arange(T)[None], T, key_valid=kv)
+    o = orc.attention(q, k, v, mask, 0.5).reshape(B, T, Hq, D)
+    for t in (0, 1):
+        np.testing.assert_allclose(o[0, t, 0], v[0, :, 0].mean(0), rtol=1e-13)
+
+
+def test_causality_under_perturbation():
+    g = np.random.default_rng(35)
+    B, T, Hq, Hkv, D = 1, 12, 6, 2, 8
+    q, k, v = (g.standard_normal((B, T, H, D)) for H in (Hq, Hkv, Hkv))
+    mask = orc.attention_mask(np.arange(T)[None], T)
+    o1 = orc.attention(q, k, v, mask, 0.4)
+    t = 6
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for a in (q2, k2, v2):
+        a[:, t + 1:] = g.standard_normal(a[:, t + 1:].shape) * 10
+    o2 = orc.attention(q2, k2, v2, mask, 0.4)
+    np.testing.assert_array_equal(o1[:, : t + 1], o2[:, : t + 1])
+    assert np.max(np.abs(o1[:, t + 1:] - o2[:, t + 1:])) > 1e-3
+
+
+def test_attention_rows_matches_full_attention():
+    g = np.random.default_rng(36)
+    B, T, Hq, Hkv, D = 2, 10, 12, 4, 16
+    q, k, v = (g.standard_normal((B, T, H, D)) for H in (Hq, Hkv, Hkv))
+    pos = np.broadcast_to(np.arange(T), (B, T))
+    mask = orc.attention_mask(pos, T)
+    full = orc.attention(q, k, v, mask, 0.3).reshape(B, T, Hq, D)
+    for b, t, h in ((0, 0, 0), (1, 9, 11), (0, 4, 5), (1, 7, 2)):
+        np.testing.assert_allclose(orc.attention_rows(q, k, v, b, t, h, mask[b, t], 0.3),
+                                   full[b, t, h], rtol=1e-13, atol=1e-15)
+
+
+def test_decode_through_cache_equals_last_row_of_prefill():
+    """Incremental decode at step T-1 reproduces row T-1 of a full causal prefill."""
+    g = np.random.default_rng(37)
+    B, T, Hq, Hkv, D, Tmax = 2, 9, 12, 2, 16, 16
+    q, k, v = (g.standard_normal((B, T, H, D)) for H in (Hq, Hkv, Hkv))
+    pos = np.broadcast_to(np.arange(T), (B, T))
+    qr, kr = orc.rope(q, pos), orc.rope(k, pos)
+    full = orc.attention(qr, kr, v, orc.attention_mask(pos, T), 0.25)
+    kc = g.standard_normal((B, Tmax, Hkv, D)) * 5  # garbage beyond the prefix
+    vc = g.standard_normal((B, Tmax, Hkv, D)) * 5
+    kc[:, : T - 1], vc[:, : T - 1] = kr[:, : T - 1], v[:, : T - 1]
+    step = np.full(B, T - 1, np.int32)
+    o, kc2, vc2, ns = orc.decode_step(kc, vc, q[:, -1:], k[:, -1:], v[:, -1:], step, 0.25, io=None)
+    np.testing.assert_array_equal(ns, T)
+    np.testing.assert_allclose(o[:, 0], full[:, -1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(kc2[:, T - 1], kr[:, -1], rtol=1e-15)
+
+
+def test_sublayer_zero_output_projection_is_identity_and_unit_rms_update():
+    g = np.random.default_rng(38)
+    B, T, d, Hq, Hkv, D = 1, 5, 32, 4, 2, 8
+    p = gi.make_sublayer_inputs(B, T, d, Hq, Hkv, D, seed=5)
+    x = orc.bf16_bits_to_f64(p["x"])
+    args = (p["wq"], p["sq"], p["wk"], p["sk"], p["wv"], p["sv"])
+    y0 = orc.sublayer(x, *args, np.zeros_like(p["wo"]), p["so"], Hq, Hkv, D, 1 / math.sqrt(D))
+    np.testing.assert_array_equal(y0, x)
+    y = orc.sublayer(x, *args, p["wo"], np.full(d, 0.5, np.float32), Hq, Hkv, D,
+                     1 / math.sqrt(D), io=None)
+    upd = y - x
+    np.testing.assert_allclose(np.sqrt(np.mean(upd * upd, -1)), 1.0, rtol=1e-6)
+    del g
