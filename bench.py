@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the Grok-1 attention core on one MI355X.
+
+Default run (N=1): the headline workload is the 8k causal prefill
+(B=1, T=8192, 48 query heads on 8 KV heads, head size 128, bf16): one step is
+RoPE of Q and K plus the causal GQA attention, and ``value`` is its
+algorithmic TFLOP/s (4*D*Hq*B*T(T+1)/2 flop per step: QK^T and P.V over the
+causal lower triangle, diagonal included). The same JSON line carries the
+decode workloads (single-token decode on a full 8192-slot cache; 32 ragged
+sequences) as KV GB/s, the full sub-layer as TFLOP/s, the roofline of the
+dominant kernel, and the fp64 CPU oracle timed on a bounded sample.
+
+Inputs are synthetic, seeded, and resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA attn prefill TFLOP/s + decode KV GB/s (48q/8kv/d128), % of roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="", help="comma list of c2,c3,c4,c5 (default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gqa_attention_grok_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if the
+    kernel sources are unchanged since the counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_steps(torch, fn, steps, warmup, inner=None):
+    """Warm up, then time `steps` calls of fn() between two synchronisations.
+    `inner(i)` (optional) returns (start_event, end_event) pairs recorded around
+    the dominant kernel inside step i."""
+    for _ in range(warmup):
+        fn(-1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def bench_prefill(torch, grok, pipe, U, gi, steps, warmup):
+    w = gi.WORKLOADS["c3_prefill_t8192"]
+    p = gi.make_workload(w.name)
+    st = pipe.PrefillStep(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), w.attn_mult,
+                          w.softcap)
+    del p
+    flop = 4 * w.D * w.Hq * w.B * w.T * (w.T + 1) // 2
+    ev = []
+
+    def step(i):
+        st.rope()
+        if i >= 0:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            st.attend()
+            e.record()
+            ev.append((s, e))
+        else:
+            st.attend()
+
+    sec = time_steps(torch, step, steps, warmup)
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    return {
+        "workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12, "unit": "TFLOP/s",
+        "flop_per_step": flop, "kernel": "prefill_mfma_kernel", "kernel_ms": kern_ms,
+        "kernel_tflops": flop / (kern_ms * 1e-3) / 1e12,
+    }
+
+
+def bench_decode(torch, grok, pipe, U, gi, name, steps, warmup, replicas):
+    """One step = RoPE + append of the new token, then split-K decode attention.
+    `replicas` copies of the cache are cycled so the working set exceeds the
+    256 MB last-level cache and each step streams K/V from HBM."""
+    w = gi.WORKLOADS[name]
+    p = gi.make_workload(name)
+    kc0, vc0 = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    reps = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(replicas - 1)]
+    q, kn, vn, stp = U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]), U.dev(p["step"])
+    steps_obj = [pipe.DecodeStep(kc, vc, q, kn, vn, stp, w.attn_mult, w.softcap) for kc, vc in reps]
+    L = p["kv_len"].astype(np.int64)
+    D, Hq, Hkv = w.D, w.Hq, w.Hkv
+    # algorithmic bytes: valid K and V rows once, q, the new k/v row, the output
+    kv_bytes = int(L.sum()) * Hkv * D * 2 * 2
+    io_bytes = w.B * (Hq * D * 2 + 2 * Hkv * D * 2 + Hq * D * 2)
+    nbytes = kv_bytes + io_bytes
+    ev = []
+
+    def step(i):
+        s_ = steps_obj[(i if i >= 0 else 0) % len(steps_obj)]
+        grok.grok_kv_append(s_.k_cache, s_.v_cache, s_.k_new, s_.v_new, s_.step, q_inout=s_.q,
+                            new_step=s_.kv_len, status=s_.status, rope_base=s_.rope_base)
+        if i >= 0:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        grok.grok_attn_decode(s_.q, s_.k_cache, s_.v_cache, s_.kv_len, s_.out, s_.workspace,
+                              s_.attn_mult, s_.softcap, status=s_.status)
+        if i >= 0:
+            b.record()
+            ev.append((a, b))
+
+    sec = time_steps(torch, step, steps, warmup)
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return {
+        "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",
+        "bytes_per_step": nbytes, "kernel": "decode_split_kernel+decode_combine_kernel",
+        "kernel_ms": kern_ms, "kernel_gbs": nbytes / (kern_ms * 1e-3) / 1e9,
+        "kernel_frac_of_hbm_peak": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "cache_replicas": replicas,
+    }
+
+
+def bench_sublayer(torch, grok, pipe, U, gi, steps, warmup):
+    w = gi.WORKLOADS["c5_sublayer_b4_t2048"]
+    p = gi.make_workload(w.name)
+    dv = {k: (U.dev_bf16(v) if k == "x" else U.dev(v)) for k, v in p.items()}
+    del p
+    st = pipe.SublayerStep(dv["x"], dv["wq"], dv["sq"], dv["wk"], dv["sk"], dv["wv"], dv["sv"], dv["wo"],
+                           dv["so"], w.Hq, w.Hkv, w.D, w.attn_mult, w.softcap, w.eps)
+    M, d = w.B * w.T, w.d_model
+    proj = 2 * M * d * (w.Hq * w.D + 2 * w.Hkv * w.D) + 2 * M * (w.Hq * w.D) * d
+    attn = 4 * w.D * w.Hq * w.B * w.T * (w.T + 1) // 2
+    flop = proj + attn
+    sec = time_steps(torch, lambda i: st(), steps, warmup)
+    return {"workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12,
+            "unit": "TFLOP/s", "flop_per_step": flop}
+
+
+def cpu_baseline(gi, orc):
+    """The fp64 oracle on a bounded sample of the 8k prefill: all 48 heads of
+    `n` query rows spread over the sequence (RoPE of the sampled q rows and of
+    all keys, then the causal softcapped attention of those rows)."""
+    w = gi.WORKLOADS["c3_prefill_t8192"]
+    p = gi.make_workload(w.name)
+    T = w.T
+    rows = np.linspace(0, T - 1, 48).astype(np.int64)
+    t0 = time.perf_counter()
+    k = orc.rope(orc.bf16_bits_to_f64(p["k"]), np.arange(T)[None], out="bf16")
+    v = orc.bf16_bits_to_f64(p["v"])
+    q = orc.rope(orc.bf16_bits_to_f64(p["q"][:, rows]), rows[None], out="bf16")
+    mask = orc.attention_mask(rows[None], T)
+    for c in range(0, len(rows), 8):  # bounded memory: 8 rows at a time
+        orc.attention(q[:, c:c + 8], k, v, mask[:, c:c + 8], w.attn_mult, w.softcap, out="bf16")
+    sec = time.perf_counter() - t0
+    flop = int(sum(4 * w.D * w.Hq * (int(t) + 1) for t in rows))
+    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} of {T} query rows (all 48 heads) of the 8k prefill, "
+                      f"incl. RoPE of all keys; {flop} flop in {sec:.1f} s, single-threaded NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention core shards with no exchange over KV heads: see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gqa_attention_grok_amd as grok
+    import gqa_attention_grok_amd.pipeline as pipe
+    import gqa_inputs as gi
+    import gpu_util as U
+
+    only = set(args.only.split(",")) if args.only else {"c2", "c3", "c4", "c5"}
+    res = {}
+    if "c3" in only:
+        res["c3"] = bench_prefill(torch, grok, pipe, U, gi, args.steps, args.warmup)
+        print(f"# c3 done: {res['c3']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "c2" in only:
+        res["c2"] = bench_decode(torch, grok, pipe, U, gi, "c2_decode_b1", args.steps, args.warmup, 16)
+        print(f"# c2 done: {res['c2']['value']:.1f} GB/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "c4" in only:
+        res["c4"] = bench_decode(torch, grok, pipe, U, gi, "c4_decode_ragged_b32", args.steps,
+                                 args.warmup, 2)
+        print(f"# c4 done: {res['c4']['value']:.1f} GB/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "c5" in only:
+        res["c5"] = bench_sublayer(torch, grok, pipe, U, gi, max(1, args.steps // 4), min(args.warmup, 2))
+        print(f"# c5 done: {res['c5']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    head = res.get("c3") or next(iter(res.values()))
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 3),
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["workload"] + (
+            ": causal GQA prefill B=1 T=8192 Hq=48 Hkv=8 D=128 bf16, step = RoPE(Q,K) + attention"
+            if head is res.get("c3") else "")},
+    }
+    if head is res.get("c3"):
+        tr = traffic_for(head["kernel"])
+        line["roofline"] = {
+            "kernel": head["kernel"], "bound": "mfma", "achieved": round(head["kernel_tflops"], 3),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": tr, "kernel_ms": round(head["kernel_ms"], 4),
+        }
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        line["cpu_baseline"] = cpu_baseline(gi, orc)
+    line["secondary"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                         for k, r in res.items() if r is not head}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""Python binding of ``libgrokattn.so`` (the gfx950 Grok-1 attention core).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream of torch to the C ABI declared in
+``include/grok_attn.h`` and raises ``GrokError`` on a non-zero status. All
+computation happens in the library's HIP kernels; there is no fallback. If
+the shared library has not been built, importing this package raises.
+
+Tensors are torch tensors on the GPU: bf16 data as ``torch.bfloat16``, fp32
+as ``torch.float32``, int8 weights as ``torch.int8``, positions/lengths as
+``torch.int32``, key masks as ``torch.uint8``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GrokError", "LIB_PATH", "lib", "GROK_BF16", "GROK_F32",
+    "grok_abi_version", "grok_status_string", "grok_last_error",
+    "grok_rmsnorm", "grok_linear_int8", "grok_rope", "grok_kv_append",
+    "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_workspace_bytes",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrokattn.so")
+GROK_BF16, GROK_F32 = 0, 1
+GROK_OK, GROK_EHIP, GROK_ENOMEM, GROK_EINVAL, GROK_ERANGE = 0, -5, -12, -22, -34
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m gqa_attention_grok_amd.build` "
+        "(there is no non-HIP fallback)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_PROTOS = {
+    "grok_abi_version": (_i, []),
+    "grok_status_string": (ctypes.c_char_p, [_i]),
+    "grok_last_error": (ctypes.c_char_p, []),
+    "grok_rmsnorm": (_i, [_p, _p, _p, _p, _i64, _i, _f, _i, _p]),
+    "grok_linear_int8": (_i, [_p, _p, _p, _p, _i64, _i, _i, _p]),
+    "grok_rope": (_i, [_p, _i, _i, _i, _i, _p, _f, _i, _p]),
+    "grok_kv_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
+    "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
+    "grok_attn_decode": (_i, [_p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i, _f, _f, _p]),
+    "grok_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+}
+for _name, (_res, _args) in _PROTOS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class GrokError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.grok_last_error().decode() or lib.grok_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != GROK_OK:
+        raise GrokError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return GROK_BF16
+    if t.dtype == torch.float32:
+        return GROK_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def grok_abi_version() -> int:
+    return lib.grok_abi_version()
+
+
+def grok_status_string(status: int) -> str:
+    return lib.grok_status_string(status).decode()
+
+
+def grok_last_error() -> str:
+    return lib.grok_last_error().decode()
+
+
+def grok_rmsnorm(x, y, gamma=None, residual=None, eps=1e-5):
+    """y[..., d] = [residual +] gamma * x / sqrt(mean(x^2) + eps) over the last axis."""
+    _need(x, "x")
+    _need(y, "y", x.dtype)
+    _need(gamma, "gamma", torch.float32)
+    _need(residual, "residual", x.dtype)
+    d = x.shape[-1]
+    _check(lib.grok_rmsnorm(_ptr(x), _ptr(gamma), _ptr(residual), _ptr(y), x.numel() // d, d,
+                            eps, _dtype_code(x), _stream(x)), "grok_rmsnorm")
+    return y
+
+
+def grok_linear_int8(x, w, scales, y):
+    """y [M, N] = x [M, K] @ (w [K, N] int8 * scales [N])."""
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.int8, 2)
+    _need(scales, "scales", torch.float32, 1)
+    _need(y, "y", torch.bfloat16)
+    K, N = w.shape
+    _check(lib.grok_linear_int8(_ptr(x), _ptr(w), _ptr(scales), _ptr(y), x.numel() // K, K, N,
+                                _stream(x)), "grok_linear_int8")
+    return y
+
+
+def grok_rope(x, offset=None, base=10000.0):
+    """In-place RoPE of x [B, T, H, D] at positions offset[b] + t."""
+    _need(x, "x", ndim=4)
+    _need(offset, "offset", torch.int32, 1)
+    B, T, H, D = x.shape
+    _check(lib.grok_rope(_ptr(x), B, T, H, D, _ptr(offset), base, _dtype_code(x), _stream(x)),
+           "grok_rope")
+    return x
+
+
+def grok_kv_append(k_cache, v_cache, k_new, v_new, step, q_inout=None, new_step=None,
+                   status=None, rope_base=10000.0):
+    """RoPE q/k at step[b] + t, write k/v into the caches at that slot."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(q_inout, "q_inout", torch.bfloat16, 4)
+    _need(step, "step", torch.int32, 1)
+    _need(new_step, "new_step", torch.int32, 1)
+    _need(status, "status", torch.int32)
+    B, Tmax, Hkv, D = k_cache.shape
+    T = k_new.shape[1]
+    Hq = q_inout.shape[2] if q_inout is not None else 0
+    _check(lib.grok_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(q_inout),
+                              _ptr(step), _ptr(new_step), _ptr(status), B, T, Tmax, Hq, Hkv, D,
+                              rope_base, _stream(k_cache)), "grok_kv_append")
+
+
+def grok_attn_prefill(q, k, v, out, attn_mult, softcap=30.0, key_valid=None):
+    """Causal GQA: q [B,T,Hq,D], k/v [B,kv_rows,Hkv,D] (kv_rows >= T), out [B,T,Hq*D]."""
+    _need(q, "q", ndim=4)
+    _need(k, "k", q.dtype, 4)
+    _need(v, "v", q.dtype, 4)
+    _need(out, "out", q.dtype)
+    _need(key_valid, "key_valid", torch.uint8, 2)
+    B, T, Hq, D = q.shape
+    kv_rows, Hkv = k.shape[1], k.shape[2]
+    _check(lib.grok_attn_prefill(_ptr(q), _ptr(k), _ptr(v), kv_rows, _ptr(key_valid), _ptr(out),
+                                 B, T, Hq, Hkv, D, attn_mult, softcap, _dtype_code(q), _stream(q)),
+           "grok_attn_prefill")
+    return out
+
+
+def grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D) -> int:
+    return lib.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D)
+
+
+def grok_attn_decode(q, k_cache, v_cache, kv_len, out, workspace, attn_mult, softcap=30.0,
+                     status=None):
+    """One-token GQA against the cache slots [0, kv_len[b]); q [B,1,Hq,D], out [B,1,Hq*D]."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(kv_len, "kv_len", torch.int32, 1)
+    _need(out, "out", torch.bfloat16)
+    _need(workspace, "workspace")
+    _need(status, "status", torch.int32)
+    B, _, Hq, D = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.grok_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(out),
+                                _ptr(workspace), ws_bytes, _ptr(status), B, Tmax, Hq, Hkv, D,
+                                attn_mult, softcap, _stream(q)), "grok_attn_decode")
+    return out

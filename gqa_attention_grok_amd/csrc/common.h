@@ -1,0 +1,79 @@
+// Shared device helpers and internal launcher declarations of the gfx950 library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "grok_attn.h"
+
+namespace grok {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (defined in the .hip files, called by api.cpp after
+// validation). Each returns hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+struct RopeFreqs {
+  float inv[256];  // inv_freq[i] = base^(-2i/D), i < D/2 (D <= 512)
+};
+
+// Correctly rounded fp32 of base^(-2i/D) for i < D/2 (computed in double).
+void rope_build_freqs(int D, float base, RopeFreqs *f);
+
+hipError_t launch_rmsnorm(const void *x, const float *gamma, const void *residual, void *y,
+                          int64_t rows, int d, float eps, int dtype, hipStream_t s);
+hipError_t launch_rope(void *x, int B, int T, int H, int D, const int32_t *offset,
+                       const RopeFreqs &f, int dtype, hipStream_t s);
+hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, void *q,
+                            const int32_t *step, int32_t *new_step, int32_t *status, int B,
+                            int T, int Tmax, int Hq, int Hkv, int D, bool do_rope,
+                            const RopeFreqs &f, hipStream_t s);
+hipError_t launch_linear_int8(const void *x, const int8_t *w, const float *scales, void *y,
+                              int64_t M, int K, int N, hipStream_t s);
+hipError_t launch_prefill_generic(const void *q, const void *k, const void *v, int64_t kv_rows,
+                                  const uint8_t *key_valid, void *out, int B, int T, int Hq,
+                                  int Hkv, int D, float mult, float cap, int dtype,
+                                  hipStream_t s);
+hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int64_t kv_rows,
+                               const uint8_t *key_valid, void *out, int B, int T, int Hq,
+                               int Hkv, float mult, float cap, hipStream_t s);
+bool prefill_mfma_supported(int Hq, int Hkv, int D, int dtype);
+hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int32_t *kv_len,
+                         void *out, void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,
+                         float mult, float cap, hipStream_t s);
+size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv);
+
+}  // namespace grok

@@ -1,0 +1,166 @@
+// C ABI entry points: host-side validation, then launch. See include/grok_attn.h
+// for the contract of every function. Validation happens before any HIP call,
+// so every error path can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return GROK_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(GROK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool bad_softmax_params(float mult, float cap) {
+  return !isfinite(mult) || !(cap > 0.f) || cap > 40.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int grok_abi_version(void) { return GROK_ABI_VERSION; }
+
+const char *grok_status_string(int status) {
+  switch (status) {
+    case GROK_OK: return "ok";
+    case GROK_EHIP: return "HIP error";
+    case GROK_ENOMEM: return "workspace too small";
+    case GROK_EINVAL: return "invalid argument";
+    case GROK_ERANGE: return "cache position out of range";
+    default: return "unknown status";
+  }
+}
+
+const char *grok_last_error(void) { return g_err; }
+
+int grok_rmsnorm(const void *x, const float *gamma, const void *residual, void *y, int64_t rows,
+                 int d, float eps, int dtype, hipStream_t stream) {
+  if (dtype != GROK_BF16 && dtype != GROK_F32) return fail(GROK_EINVAL, "rmsnorm: unknown dtype %d", dtype);
+  if (rows < 0 || d < 1) return fail(GROK_EINVAL, "rmsnorm: bad shape rows=%lld d=%d", (long long)rows, d);
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(GROK_EINVAL, "rmsnorm: bad eps");
+  if (rows == 0) return ok();
+  if (!x || !y) return fail(GROK_EINVAL, "rmsnorm: null x or y");
+  return hip_status(grok::launch_rmsnorm(x, gamma, residual, y, rows, d, eps, dtype, stream), "rmsnorm");
+}
+
+int grok_linear_int8(const void *x, const int8_t *w, const float *scales, void *y, int64_t M,
+                     int K, int N, hipStream_t stream) {
+  if (M < 0 || K < 1 || N < 1) return fail(GROK_EINVAL, "linear_int8: bad shape M=%lld K=%d N=%d", (long long)M, K, N);
+  if (K % 8 || N % 8) return fail(GROK_EINVAL, "linear_int8: K and N must be multiples of 8 (K=%d N=%d)", K, N);
+  if (M == 0) return ok();
+  if ((M + 127) / 128 > 65535) return fail(GROK_EINVAL, "linear_int8: M=%lld too large", (long long)M);
+  if (!x || !w || !scales || !y) return fail(GROK_EINVAL, "linear_int8: null pointer");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(scales)) % 16 ||
+      (reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(y)) % 8)
+    return fail(GROK_EINVAL, "linear_int8: misaligned pointer");
+  return hip_status(grok::launch_linear_int8(x, w, scales, y, M, K, N, stream), "linear_int8");
+}
+
+int grok_rope(void *x, int B, int T, int H, int D, const int32_t *offset, float base, int dtype,
+              hipStream_t stream) {
+  if (dtype != GROK_BF16 && dtype != GROK_F32) return fail(GROK_EINVAL, "rope: unknown dtype %d", dtype);
+  if (B < 0 || T < 0 || H < 0 || D < 2) return fail(GROK_EINVAL, "rope: bad shape");
+  if (D % 2 || D > 512) return fail(GROK_EINVAL, "rope: head size must be even and <= 512 (D=%d)", D);
+  if (!(base > 0.f) || !isfinite(base)) return fail(GROK_EINVAL, "rope: bad base");
+  if (static_cast<int64_t>(B) * T * H == 0) return ok();
+  if (!x) return fail(GROK_EINVAL, "rope: null x");
+  grok::RopeFreqs f;
+  grok::rope_build_freqs(D, base, &f);
+  return hip_status(grok::launch_rope(x, B, T, H, D, offset, f, dtype, stream), "rope");
+}
+
+int grok_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                   void *q_inout, const int32_t *step, int32_t *new_step, int32_t *status, int B,
+                   int T, int Tmax, int Hq, int Hkv, int D, float rope_base, hipStream_t stream) {
+  if (B < 1 || T < 1 || Tmax < 1 || Hkv < 1 || D < 2) return fail(GROK_EINVAL, "kv_append: bad shape");
+  if (T > Tmax) return fail(GROK_EINVAL, "kv_append: T=%d exceeds Tmax=%d", T, Tmax);
+  if (D % 16 || D > 512) return fail(GROK_EINVAL, "kv_append: head size must be a multiple of 16, <= 512 (D=%d)", D);
+  if (q_inout && (Hq < 1 || Hq % Hkv)) return fail(GROK_EINVAL, "kv_append: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (!k_cache || !v_cache || !k_new || !v_new || !step) return fail(GROK_EINVAL, "kv_append: null pointer");
+  if (!isfinite(rope_base)) return fail(GROK_EINVAL, "kv_append: bad rope_base");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+                       reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                       reinterpret_cast<uintptr_t>(q_inout);
+  if (al % 16) return fail(GROK_EINVAL, "kv_append: misaligned pointer");
+  if (static_cast<int64_t>(B) * T > 0x7fffffff) return fail(GROK_EINVAL, "kv_append: too many tokens");
+  grok::RopeFreqs f;
+  const bool do_rope = rope_base > 0.f;
+  grok::rope_build_freqs(D, do_rope ? rope_base : 1.f, &f);
+  return hip_status(grok::launch_kv_append(k_cache, v_cache, k_new, v_new, q_inout, step, new_step,
+                                           status, B, T, Tmax, Hq, Hkv, D, do_rope, f, stream),
+                    "kv_append");
+}
+
+int grok_attn_prefill(const void *q, const void *k, const void *v, int64_t kv_rows,
+                      const uint8_t *key_valid, void *out, int B, int T, int Hq, int Hkv, int D,
+                      float attn_mult, float softcap, int dtype, hipStream_t stream) {
+  if (dtype != GROK_BF16 && dtype != GROK_F32) return fail(GROK_EINVAL, "attn_prefill: unknown dtype %d", dtype);
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1) return fail(GROK_EINVAL, "attn_prefill: bad shape");
+  if (Hq % Hkv) return fail(GROK_EINVAL, "attn_prefill: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (kv_rows < T) return fail(GROK_EINVAL, "attn_prefill: kv_rows=%lld < T=%d", (long long)kv_rows, T);
+  if (D % 8 || D > 256) return fail(GROK_EINVAL, "attn_prefill: head size must be a multiple of 8, <= 256 (D=%d)", D);
+  if (bad_softmax_params(attn_mult, softcap))
+    return fail(GROK_EINVAL, "attn_prefill: attn_mult must be finite and softcap in (0, 40]");
+  if (!q || !k || !v || !out) return fail(GROK_EINVAL, "attn_prefill: null pointer");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
+  if (grok::prefill_mfma_supported(Hq, Hkv, D, dtype)) {
+    if (al % 16) return fail(GROK_EINVAL, "attn_prefill: misaligned pointer");
+    return hip_status(grok::launch_prefill_mfma(q, k, v, kv_rows, key_valid, out, B, T, Hq, Hkv,
+                                                attn_mult, softcap, stream),
+                      "attn_prefill");
+  }
+  return hip_status(grok::launch_prefill_generic(q, k, v, kv_rows, key_valid, out, B, T, Hq, Hkv, D,
+                                                 attn_mult, softcap, dtype, stream),
+                    "attn_prefill");
+}
+
+size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D) {
+  if (B < 1 || Tmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D != 128) return 0;
+  return grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);
+}
+
+int grok_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *kv_len, void *out, void *workspace, size_t ws_bytes,
+                     int32_t *status, int B, int Tmax, int Hq, int Hkv, int D, float attn_mult,
+                     float softcap, hipStream_t stream) {
+  if (B < 1 || Tmax < 1 || Hq < 1 || Hkv < 1) return fail(GROK_EINVAL, "attn_decode: bad shape");
+  if (Hq % Hkv) return fail(GROK_EINVAL, "attn_decode: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(GROK_EINVAL, "attn_decode: at most 16 query heads per KV head");
+  if (D != 128) return fail(GROK_EINVAL, "attn_decode: head size must be 128 (D=%d)", D);
+  if (bad_softmax_params(attn_mult, softcap))
+    return fail(GROK_EINVAL, "attn_decode: attn_mult must be finite and softcap in (0, 40]");
+  if (!q || !k_cache || !v_cache || !kv_len || !out || !workspace)
+    return fail(GROK_EINVAL, "attn_decode: null pointer");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(workspace);
+  if (al % 16) return fail(GROK_EINVAL, "attn_decode: misaligned pointer");
+  const size_t need = grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);
+  if (ws_bytes < need)
+    return fail(GROK_ENOMEM, "attn_decode: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (static_cast<int64_t>(B) * Hq > 0x7fffffff || B > 65535) return fail(GROK_EINVAL, "attn_decode: batch too large");
+  return hip_status(grok::launch_decode(q, k_cache, v_cache, kv_len, out, workspace, status, B, Tmax,
+                                        Hq, Hkv, attn_mult, softcap, stream),
+                    "attn_decode");
+}
+
+}  // extern "C"

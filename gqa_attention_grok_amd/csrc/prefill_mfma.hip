@@ -1,0 +1,318 @@
+// Causal grouped-query flash attention for prefill on gfx950 bf16 MFMA, D = 128.
+//
+// Method (Grok-1 walkthrough, ch. 4 "model.py close reading, part 1", §4.5.2 to
+// §4.5.4; mask from ch. 6 "model.py close reading, part 3", §6.4.2):
+//   z = mult * <q_i, k_j>, c = cap*tanh(z/cap), masked -> -1e30, softmax, P.V.
+//
+// Work decomposition
+//   A workgroup (4 waves) owns 12 "row blocks" of 16 query rows. A row block is
+//   16 consecutive positions of one query head. The 12 blocks are Gc heads of
+//   one KV group x (12/Gc) position blocks, so every K/V tile staged in LDS is
+//   used by all those heads (for Grok-1's 6:1 grouping: 6 heads x 32 positions).
+//   Each wave owns 3 row blocks and walks the causal key range in tiles of 32.
+//
+// MFMA formulation (v_mfma_f32_16x16x32_bf16), transposed so that each lane
+// always holds data of query row (lane % 16):
+//   S^T[key, row]  = K[key, :] . Q[row, :]^T          A = K (LDS), B = Q (regs)
+//   O^T[d, row]   += V^T[d, key] . P^T[key, row]      A = V^T (LDS), B = P (regs)
+//   The K rows feeding S^T are permuted so that the S^T accumulator of lane l
+//   holds keys 8*(l/16) .. 8*(l/16)+7 for its row -- exactly the B-operand
+//   layout P needs for the P.V product, so P never leaves registers.
+//
+// Softmax without a running max: after the softcap every unmasked logit lies in
+// [-cap, cap], so p = exp(c - cap) is in [exp(-2cap), 1] -- no overflow, and no
+// underflow below fp32/bf16 normals for cap <= 40. Softmax is shift-invariant,
+// so this is the same distribution as the max-subtracted form, without the
+// per-tile max reduction and rescaling of O. With r = 1/(1+exp(2z/cap)):
+//   c - cap = -2*cap*r,   p = exp2(-2*cap*log2(e) * r).
+// Masked logits give p = 0 exactly. A row with no unmasked key (only possible
+// with key padding) takes the -1e30 semantics of the pages: the uniform mean
+// of all T value rows, computed in the epilogue for such rows only.
+#include "common.h"
+
+namespace grok {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kRB = 3;             // row blocks per wave
+constexpr int kRowBlocks = kWaves * kRB;
+constexpr int kBN = 32;            // keys per tile
+constexpr int kKRow = kD + 8;      // padded LDS row of K (bf16 elements)
+constexpr int kVRow = kBN + 8;     // padded LDS row of V^T (bf16 elements)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  f32x2 f = {a, b};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+struct PrefillArgs {
+  const bf16_t *q, *k, *v;
+  const uint8_t *key_valid;
+  bf16_t *out;
+  int64_t kv_rows;
+  int B, T, Hq, Hkv, G, Gc, npb, nhc, nqt;
+  float k1, k2;  // exp2 scale inside the softcap, outer exp2 scale
+};
+
+template <bool kHasValid>
+__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kBN][kKRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][kD][kVRow];
+  __shared__ uint8_t kvs[2][kBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int lr = lane % 16;  // this lane's row inside a row block
+  const int lg = lane / 16;  // this lane's k/key group
+
+  // blockIdx -> (g, head chunk, query tile (longest first), batch); g fastest so
+  // that, with 8 KV heads, all tiles of one KV head land on one XCD's L2.
+  int id = blockIdx.x;
+  const int g = id % a.Hkv;
+  id /= a.Hkv;
+  const int hc = id % a.nhc;
+  id /= a.nhc;
+  const int qt = a.nqt - 1 - (id % a.nqt);
+  const int b = id / a.nqt;
+  const int span = 16 * a.npb;
+  const int p0 = qt * span;
+  const int kend = min(a.T, p0 + span);
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  // This wave's row blocks.
+  int head[kRB], pos[kRB];
+  int wmin = 1 << 30, wmax = -1;
+#pragma unroll
+  for (int i = 0; i < kRB; ++i) {
+    const int r = wave * kRB + i;
+    head[i] = g * a.G + hc * a.Gc + (r % a.Gc);
+    const int pb = r / a.Gc;
+    pos[i] = p0 + 16 * pb + lr;
+    wmin = min(wmin, p0 + 16 * pb);
+    wmax = max(wmax, p0 + 16 * pb + 15);
+  }
+  wmax = min(wmax, a.T - 1);
+
+  // Q fragments (B operand of S^T): row lr, dims 32*kk + 8*lg .. +8.
+  bf16x8 qf[kRB][4];
+#pragma unroll
+  for (int i = 0; i < kRB; ++i) {
+    const bool ok = pos[i] < a.T;
+    const bf16_t *qp = a.q + ((static_cast<int64_t>(b) * a.T + (ok ? pos[i] : 0)) * a.Hq + head[i]) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 w = ok ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * lg) : u32x4{0, 0, 0, 0};
+      qf[i][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x4 oacc[kRB][8];
+#pragma unroll
+  for (int i = 0; i < kRB; ++i)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum[kRB] = {0.f, 0.f, 0.f};
+
+  // Tile loader: K chunks (2 per thread), V key pairs (2 rows x 16 B per thread).
+  const bf16_t *kbase = a.k + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
+  const bf16_t *vbase = a.v + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
+  const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
+  const int kc0 = tid, kc1 = tid + kThreads;  // chunk ids: key = id/16, dchunk = id%16
+  const int vm = tid / 16, vc = tid % 16;     // V: keys 2vm, 2vm+1; dims 8vc..8vc+7
+  u32x4 kr0, kr1, vr0, vr1;
+  uint8_t kvr = 0;
+
+  auto gload = [&](int key0) {
+    const int k0 = key0 + kc0 / 16, k1 = key0 + kc1 / 16;
+    kr0 = k0 < a.T ? *reinterpret_cast<const u32x4 *>(kbase + k0 * rstride + (kc0 % 16) * 8) : u32x4{0, 0, 0, 0};
+    kr1 = k1 < a.T ? *reinterpret_cast<const u32x4 *>(kbase + k1 * rstride + (kc1 % 16) * 8) : u32x4{0, 0, 0, 0};
+    const int v0 = key0 + 2 * vm, v1 = v0 + 1;
+    vr0 = v0 < a.T ? *reinterpret_cast<const u32x4 *>(vbase + v0 * rstride + vc * 8) : u32x4{0, 0, 0, 0};
+    vr1 = v1 < a.T ? *reinterpret_cast<const u32x4 *>(vbase + v1 * rstride + vc * 8) : u32x4{0, 0, 0, 0};
+    if constexpr (kHasValid) {
+      if (tid < kBN) kvr = (key0 + tid < a.T) ? a.key_valid[static_cast<int64_t>(b) * a.T + key0 + tid] : 0;
+    }
+  };
+  auto lstore = [&](int buf) {
+    *reinterpret_cast<u32x4 *>(&Ks[buf][kc0 / 16][(kc0 % 16) * 8]) = kr0;
+    *reinterpret_cast<u32x4 *>(&Ks[buf][kc1 / 16][(kc1 % 16) * 8]) = kr1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w0 = vr0[e], w1 = vr1[e];
+      // dims 8vc+2e (low halves) and 8vc+2e+1 (high halves) of keys 2vm, 2vm+1
+      *reinterpret_cast<uint32_t *>(&Vt[buf][8 * vc + 2 * e][2 * vm]) = (w0 & 0xffffu) | (w1 << 16);
+      *reinterpret_cast<uint32_t *>(&Vt[buf][8 * vc + 2 * e + 1][2 * vm]) = (w0 >> 16) | (w1 & 0xffff0000u);
+    }
+    if constexpr (kHasValid) {
+      if (tid < kBN) kvs[buf][tid] = kvr;
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int key0 = t * kBN;
+    if (t + 1 < ntiles) gload(key0 + kBN);
+
+    if (key0 <= wmax) {
+      // S^T for the 3 row blocks; K operand row for block kb:
+      //   key = 8*(lr/4) + 4*kb + (lr%4)  ->  acc slot v of lane l is key 8*lg + 4*kb + v.
+      f32x4 sacc[kRB][2];
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) sacc[i][0] = sacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int krow = 8 * (lr / 4) + 4 * kb + (lr % 4);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ks[buf][krow][32 * kk + 8 * lg]);
+#pragma unroll
+          for (int i = 0; i < kRB; ++i)
+            sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[i][kk], sacc[i][kb], 0, 0, 0);
+        }
+      }
+      // softcap + shifted exp -> P (bf16) in the B-operand layout of P.V.
+      const bool diag = key0 + kBN - 1 > wmin;
+      bf16x8 pf[kRB];
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float s = sacc[i][e >> 2][e & 3];
+          const float ex = __builtin_amdgcn_exp2f(s * a.k1);
+          const float r = __builtin_amdgcn_rcpf(1.f + ex);
+          p[e] = __builtin_amdgcn_exp2f(a.k2 * r);
+        }
+        if (diag || kHasValid) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = key0 + 8 * lg + e;
+            bool ok = key <= pos[i];
+            if constexpr (kHasValid) ok = ok && kvs[buf][8 * lg + e] != 0;
+            p[e] = ok ? p[e] : 0.f;
+          }
+        }
+        u32x4 w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                   cvt_pk_bf16(p[6], p[7])};
+        // The row sum adds the bf16-rounded weights that the P.V product uses,
+        // so the normalised weights of a row sum to one.
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ls += lo_bf16(w[e]) + hi_bf16(w[e]);
+        lsum[i] += ls;
+        pf[i] = __builtin_bit_cast(bf16x8, w);
+      }
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[buf][16 * db + lr][8 * lg]);
+#pragma unroll
+        for (int i = 0; i < kRB; ++i)
+          oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], oacc[i][db], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: row sums across the 4 lane groups, normalise, store bf16.
+#pragma unroll
+  for (int i = 0; i < kRB; ++i) {
+    float l = lsum[i];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (pos[i] >= a.T) continue;
+    bf16_t *orow = a.out + ((static_cast<int64_t>(b) * a.T + pos[i]) * a.Hq + head[i]) * kD;
+    if (kHasValid && l == 0.f) {
+      // No valid key for this row: equal weights on all T value rows.
+      f32x4 acc[8];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < a.T; ++j) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const u32x2 w = *reinterpret_cast<const u32x2 *>(vbase + j * rstride + 16 * db + 4 * lg);
+          acc[db][0] += lo_bf16(w[0]);
+          acc[db][1] += hi_bf16(w[0]);
+          acc[db][2] += lo_bf16(w[1]);
+          acc[db][3] += hi_bf16(w[1]);
+        }
+      }
+      const float invt = 1.f / static_cast<float>(a.T);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int d = 16 * db + 4 * lg;
+        u32x2 w = {cvt_pk_bf16(acc[db][0] * invt, acc[db][1] * invt),
+                   cvt_pk_bf16(acc[db][2] * invt, acc[db][3] * invt)};
+        *reinterpret_cast<u32x2 *>(orow + d) = w;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d = 16 * db + 4 * lg;
+      const f32x4 o = oacc[i][db];
+      u32x2 w = {cvt_pk_bf16(o[0] / l, o[1] / l), cvt_pk_bf16(o[2] / l, o[3] / l)};
+      *reinterpret_cast<u32x2 *>(orow + d) = w;
+    }
+  }
+}
+
+int pick_gc(int G) {
+  for (int c = 12; c >= 1; --c)
+    if (G % c == 0 && 12 % c == 0) return c;
+  return 1;
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(int Hq, int Hkv, int D, int dtype) {
+  return dtype == GROK_BF16 && D == kD && Hkv > 0 && Hq % Hkv == 0;
+}
+
+hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int64_t kv_rows,
+                               const uint8_t *key_valid, void *out, int B, int T, int Hq,
+                               int Hkv, float mult, float cap, hipStream_t s) {
+  PrefillArgs a;
+  a.q = static_cast<const bf16_t *>(q);
+  a.k = static_cast<const bf16_t *>(k);
+  a.v = static_cast<const bf16_t *>(v);
+  a.key_valid = key_valid;
+  a.out = static_cast<bf16_t *>(out);
+  a.kv_rows = kv_rows;
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Gc = pick_gc(a.G);
+  a.npb = kRowBlocks / a.Gc;
+  a.nhc = a.G / a.Gc;
+  a.nqt = (T + 16 * a.npb - 1) / (16 * a.npb);
+  a.k1 = 2.f * mult * kLog2e / cap;
+  a.k2 = -2.f * cap * kLog2e;
+  const int64_t nblk = static_cast<int64_t>(B) * Hkv * a.nhc * a.nqt;
+  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (key_valid)
+    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace grok

@@ -1,0 +1,102 @@
+"""The hot path as sequences of C-ABI calls on preallocated device buffers.
+
+Nothing here computes: each step only orders calls into ``libgrokattn.so`` on
+the current stream, with every output buffer allocated once up front (torch
+owns device memory).
+
+* ``DecodeStep``   -- one decoded token per sequence (Grok-1 walkthrough, ch. 4
+  "model.py close reading, part 1", §4.4): RoPE q and the new k at step[b],
+  append k/v to the cache, attend slots [0, step[b]+1).
+* ``PrefillStep``  -- a prompt with no cache (same page, §4.3.1 and §4.5):
+  RoPE q and k at positions 0..T-1, causal GQA attention.
+* ``SublayerStep`` -- the attention half of a decoder layer (ch. 6 "model.py
+  close reading, part 3", §6.3.1): h = x + norm(Wo . attn(rope(Wq n),
+  rope(Wk n), Wv n)) with n = norm(x).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (grok_attn_decode, grok_attn_decode_workspace_bytes, grok_attn_prefill,
+               grok_kv_append, grok_linear_int8, grok_rmsnorm, grok_rope)
+
+
+class DecodeStep:
+    def __init__(self, k_cache, v_cache, q, k_new, v_new, step, attn_mult, softcap=30.0,
+                 rope_base=10000.0):
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.q, self.k_new, self.v_new, self.step = q, k_new, v_new, step
+        self.attn_mult, self.softcap, self.rope_base = attn_mult, softcap, rope_base
+        B, Tmax, Hkv, D = k_cache.shape
+        Hq = q.shape[2]
+        dev = q.device
+        self.out = torch.empty((B, 1, Hq * D), dtype=torch.bfloat16, device=dev)
+        self.kv_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        nbytes = grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D)
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+    def __call__(self):
+        grok_kv_append(self.k_cache, self.v_cache, self.k_new, self.v_new, self.step,
+                       q_inout=self.q, new_step=self.kv_len, status=self.status,
+                       rope_base=self.rope_base)
+        grok_attn_decode(self.q, self.k_cache, self.v_cache, self.kv_len, self.out,
+                         self.workspace, self.attn_mult, self.softcap, status=self.status)
+        return self.out
+
+
+class PrefillStep:
+    def __init__(self, q, k, v, attn_mult, softcap=30.0, rope_base=10000.0, key_valid=None):
+        self.q, self.k, self.v = q, k, v
+        self.attn_mult, self.softcap, self.rope_base = attn_mult, softcap, rope_base
+        self.key_valid = key_valid
+        B, T, Hq, D = q.shape
+        self.out = torch.empty((B, T, Hq * D), dtype=q.dtype, device=q.device)
+
+    def rope(self):
+        grok_rope(self.q, None, self.rope_base)
+        grok_rope(self.k, None, self.rope_base)
+
+    def attend(self):
+        return grok_attn_prefill(self.q, self.k, self.v, self.out, self.attn_mult, self.softcap,
+                                 key_valid=self.key_valid)
+
+    def __call__(self):
+        self.rope()
+        return self.attend()
+
+
+class SublayerStep:
+    """Attention sub-layer with unit-scale norms and int8 projections."""
+
+    def __init__(self, x, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D, attn_mult, softcap=30.0,
+                 eps=1e-5, rope_base=10000.0, key_valid=None):
+        self.x = x
+        self.w = (wq, sq, wk, sk, wv, sv, wo, so)
+        self.Hq, self.Hkv, self.D = Hq, Hkv, D
+        self.attn_mult, self.softcap, self.eps, self.rope_base = attn_mult, softcap, eps, rope_base
+        self.key_valid = key_valid
+        B, T, d = x.shape
+        dev = x.device
+        bf = torch.bfloat16
+        self.n = torch.empty((B, T, d), dtype=bf, device=dev)
+        self.q = torch.empty((B, T, Hq, D), dtype=bf, device=dev)
+        self.k = torch.empty((B, T, Hkv, D), dtype=bf, device=dev)
+        self.v = torch.empty((B, T, Hkv, D), dtype=bf, device=dev)
+        self.attn = torch.empty((B, T, Hq * D), dtype=bf, device=dev)
+        self.o = torch.empty((B, T, d), dtype=bf, device=dev)
+        self.y = torch.empty((B, T, d), dtype=bf, device=dev)
+
+    def __call__(self):
+        wq, sq, wk, sk, wv, sv, wo, so = self.w
+        grok_rmsnorm(self.x, self.n, eps=self.eps)
+        grok_linear_int8(self.n, wq, sq, self.q)
+        grok_linear_int8(self.n, wk, sk, self.k)
+        grok_linear_int8(self.n, wv, sv, self.v)
+        grok_rope(self.q, None, self.rope_base)
+        grok_rope(self.k, None, self.rope_base)
+        grok_attn_prefill(self.q, self.k, self.v, self.attn, self.attn_mult, self.softcap,
+                          key_valid=self.key_valid)
+        grok_linear_int8(self.attn, wo, so, self.o)
+        grok_rmsnorm(self.o, self.y, residual=self.x, eps=self.eps)
+        return self.y

@@ -1,0 +1,182 @@
+/*
+ * grok_attn.h -- C ABI of the MI355X (gfx950) Grok-1 attention sub-layer core.
+ *
+ * Sources: the Grok-1 walkthrough pages
+ *   [ch4] "model.py close reading, part 1: RMSNorm, RoPE, GQA Attention"
+ *   [ch6] "model.py close reading, part 3: block assembly and sharding"
+ *   [ch3] "Configuration and hyperparameters"
+ * Section numbers below are the pages' own.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers (HIP global memory), row-major and
+ *   contiguous, owned by the caller. The library allocates nothing, keeps no
+ *   state between calls, and never synchronises: work is enqueued on `stream`
+ *   (NULL = the default stream) and the call returns.
+ * - Return value: GROK_OK (0) or a negative GROK_E* code. Arguments are
+ *   validated on the host before anything is enqueued; on an error nothing is
+ *   enqueued and grok_last_error() (thread-local) describes the problem.
+ *   GROK_EHIP means a HIP launch failed after validation.
+ * - dtype codes: GROK_BF16 (bfloat16 raw bits, 2 bytes) or GROK_F32.
+ * - Head layout: query head h uses KV head h / (Hq/Hkv) ([ch4] §4.5.2: the
+ *   queries are viewed as [B, T, Hkv, Hq/Hkv, D]); the attention output is
+ *   [B, T, Hq*D] with head h in columns h*D .. h*D+D-1 ([ch4] §4.5.4).
+ * - Device-resident integer arguments (step, kv_len) cannot be checked on the
+ *   host. Kernels check them; a bad value skips that sequence's work and, if
+ *   the optional device word `status` is non-NULL, stores GROK_ERANGE into it
+ *   (the library never clears `status`; the caller zeroes it).
+ */
+#ifndef GROK_ATTN_H
+#define GROK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GROK_API __attribute__((visibility("default")))
+
+#define GROK_ABI_VERSION 1
+
+#define GROK_OK 0
+#define GROK_EHIP (-5)     /* a HIP call failed (see grok_last_error) */
+#define GROK_ENOMEM (-12)  /* caller-provided workspace too small */
+#define GROK_EINVAL (-22)  /* bad shape, null pointer, unsupported dtype/size */
+#define GROK_ERANGE (-34)  /* a cache position is outside [0, Tmax) */
+
+#define GROK_BF16 0
+#define GROK_F32 1
+
+GROK_API int grok_abi_version(void);
+GROK_API const char *grok_status_string(int status);
+/* Description of the last error raised on the calling thread ("" if none). */
+GROK_API const char *grok_last_error(void);
+
+/*
+ * RMSNorm over the last axis ([ch4] §4.2): for each of `rows` rows of `d`
+ *   y = gamma * x / sqrt(mean(x^2) + eps)
+ * computed in fp32 and rounded to `dtype`. No mean subtraction, no bias.
+ *   x, y      [rows, d] of `dtype`; y may alias x.
+ *   gamma     [d] fp32, or NULL for the unit scale (hk_rms_norm without scale).
+ *   residual  [rows, d] of `dtype` or NULL. When given, the normalised row is
+ *             rounded to `dtype` and then added to it, rounded again:
+ *             y = residual + norm(x) -- the post-norm residual update of the
+ *             sandwich norm ([ch6] §6.3.1). y may alias residual.
+ * Errors: EINVAL if a required pointer is NULL, rows < 0, d < 1, eps < 0 or
+ * dtype unknown. rows == 0 is a no-op.
+ */
+GROK_API int grok_rmsnorm(const void *x, const float *gamma, const void *residual, void *y,
+                 int64_t rows, int d, float eps, int dtype, hipStream_t stream);
+
+/*
+ * int8-weight Linear ([ch4] §4.1, §4.1.1): y = x @ (w * scales), no bias.
+ *   x       [M, K] bf16 activations.
+ *   w       [K, N] int8 weights (input axis first, as the pages store them).
+ *   scales  [N] fp32, one per output channel (broadcast along K).
+ *   y       [M, N] bf16.
+ * The int8 values are used exactly (|w| <= 127 is exact in bf16), products are
+ * accumulated in fp32, and the channel scale is applied to the fp32 sum before
+ * rounding to bf16.
+ * Errors: EINVAL for NULL pointers, M < 0, K < 1, N < 1, or K or N not a
+ * multiple of 8. M == 0 is a no-op.
+ */
+GROK_API int grok_linear_int8(const void *x, const int8_t *w, const float *scales, void *y,
+                     int64_t M, int K, int N, hipStream_t stream);
+
+/*
+ * Rotary embedding, in place ([ch4] §4.3, §4.3.1): for x [B, T, H, D] and the
+ * position p = offset[b] + t,
+ *   inv_freq[i] = base^(-2i/D) (fp32),  theta_i = fp32(p * inv_freq[i]),
+ *   x'_i       = x_i cos theta_i - x_{i+D/2} sin theta_i
+ *   x'_{i+D/2} = x_i sin theta_i + x_{i+D/2} cos theta_i     (i < D/2)
+ * i.e. x*cos + rotate_half(x)*sin with GPT-NeoX half-split pairing. Computed
+ * in fp32, rounded to `dtype`.
+ *   offset  [B] int32 device array, or NULL for offset 0.
+ * Errors: EINVAL for NULL x, negative sizes, D odd or D > 512, base <= 0, or
+ * unknown dtype. Empty tensors are a no-op.
+ */
+GROK_API int grok_rope(void *x, int B, int T, int H, int D, const int32_t *offset, float base,
+              int dtype, hipStream_t stream);
+
+/*
+ * KV-cache append with RoPE applied first ([ch4] §4.4): for every sequence b
+ * and new token t, position p = step[b] + t:
+ *   k_cache[b, p] = rope(k_new[b, t], p)   (k_new itself is not modified)
+ *   v_cache[b, p] = v_new[b, t]            (bit copy)
+ *   q_inout[b, t] = rope(q_inout[b, t], p) (if q_inout is not NULL)
+ *   new_step[b]   = step[b] + T            (if new_step is not NULL)
+ * With rope_base <= 0 no rotation is applied (k is copied bit for bit).
+ * No other cache slot is touched. All tensors bf16:
+ *   caches [B, Tmax, Hkv, D]; k_new, v_new [B, T, Hkv, D]; q_inout [B, T, Hq, D].
+ *   step   [B] int32 device array; new_step may alias step.
+ * A sequence with step[b] < 0 or step[b] + T > Tmax is skipped entirely (no
+ * write, new_step[b] = step[b]) and GROK_ERANGE is stored to *status.
+ * Errors: EINVAL for NULL required pointers, sizes < 1 (B, T, Tmax, Hkv, D),
+ * Hq not a multiple of Hkv (when q_inout is given), D not a multiple of 16 or
+ * D > 512, T > Tmax, or a pointer not 16-byte aligned.
+ */
+GROK_API int grok_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                   void *q_inout, const int32_t *step, int32_t *new_step, int32_t *status,
+                   int B, int T, int Tmax, int Hq, int Hkv, int D, float rope_base,
+                   hipStream_t stream);
+
+/*
+ * Causal grouped-query attention over a prompt ([ch4] §4.5.2-§4.5.4,
+ * [ch6] §6.4.2). For query position i of sequence b and head h (KV head g):
+ *   z_j  = attn_mult * <q[b,i,h], k[b,j,g]>                       (fp32)
+ *   c_j  = softcap * tanh(z_j / softcap)
+ *   l_j  = c_j if (j <= i and key_valid[b,j] != 0) else -1e30
+ *   out[b,i,h*D:(h+1)*D] = sum_j softmax(l)_j * v[b,j,g]
+ * Masked logits use the pages' finite -1e30 fill: a query that sees no valid
+ * key averages all T value rows uniformly.
+ *   q    [B, T, Hq, D]; k, v [B, kv_rows, Hkv, D] where kv_rows >= T is the
+ *        per-sequence row stride (T for freshly projected K/V, Tmax when they
+ *        are read in place from a cache); only rows 0..T-1 are read.
+ *   key_valid [B, T] uint8 (1 = real token) or NULL (no padding).
+ *   out  [B, T, Hq*D], same dtype as q/k/v.
+ * dtype GROK_BF16: bf16 operands, fp32 logits/softmax/accumulation, bf16 out.
+ * dtype GROK_F32: fp32 throughout.
+ * Errors: EINVAL for NULL required pointers, sizes < 1, Hq % Hkv != 0,
+ * kv_rows < T, D > 256 or D % 8 != 0, attn_mult not finite, softcap outside
+ * (0, 40], unknown dtype, or (bf16 with D == 128) a pointer not 16-byte aligned.
+ * The softcap bound comes from the kernels' softmax: every unmasked softcapped
+ * logit lies in [-softcap, softcap], so exp(c - softcap) is used in place of
+ * the max-subtracted exponent; for softcap <= 40 its smallest value,
+ * exp(-2*softcap), stays a normal fp32/bf16 number.
+ */
+GROK_API int grok_attn_prefill(const void *q, const void *k, const void *v, int64_t kv_rows,
+                      const uint8_t *key_valid, void *out, int B, int T, int Hq, int Hkv,
+                      int D, float attn_mult, float softcap, int dtype, hipStream_t stream);
+
+/*
+ * Single-token decode attention against a KV cache ([ch4] §4.4, §4.5; the
+ * causal mask of one query is all-ones and the memory mask keeps slots
+ * j < kv_len[b]):
+ *   out[b, 0, h*D:(h+1)*D] = sum_{j < kv_len[b]} softmax_j(softcap(attn_mult *
+ *                             <q[b,0,h], k_cache[b,j,g]>)) * v_cache[b,j,g]
+ * Slots j >= kv_len[b] are never read.
+ *   q [B, 1, Hq, D]; caches [B, Tmax, Hkv, D]; kv_len [B] int32 device
+ *   (= step + 1 after the new token was appended); out [B, 1, Hq*D]; bf16.
+ *   workspace: device scratch of at least grok_attn_decode_workspace_bytes()
+ *   bytes (split partial sums); its contents need no initialisation.
+ * A sequence with kv_len[b] outside [1, Tmax] gets an all-zero output row and
+ * GROK_ERANGE is stored to *status.
+ * Errors: EINVAL for NULL pointers, sizes < 1, Hq % Hkv != 0, Hq/Hkv > 16,
+ * D != 128, bad attn_mult/softcap as for prefill; ENOMEM if ws_bytes is too
+ * small.
+ */
+GROK_API int grok_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *kv_len, void *out, void *workspace, size_t ws_bytes,
+                     int32_t *status, int B, int Tmax, int Hq, int Hkv, int D,
+                     float attn_mult, float softcap, hipStream_t stream);
+
+/* Workspace bytes grok_attn_decode needs for these sizes (0 on bad sizes). */
+GROK_API size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GROK_ATTN_H */

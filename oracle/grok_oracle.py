@@ -19,8 +19,7 @@ RoPE phase is float32 there, [ch4] §4.3.1). Results are rounded to the output
 dtype only where an exported operation hands back a tensor (``out=`` below),
 which is where the pages' code casts back to the forward dtype.
 
-Readings where the pages are silent (each is listed with its reason in the
-design notes of the repository):
+Readings where the pages are silent:
 
 * RoPE ``inv_freq[i]`` is the float32 nearest to ``base**(-2i/D)``; the phase
   ``t*inv_freq`` is one float32 product ([ch4] §4.3.1); cos/sin in float64.

@@ -1,0 +1,149 @@
+"""The C-ABI library loads, exports every declared symbol, and validates its
+arguments on the host (no GPU needed: every call below fails validation before
+anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "grok_attn.h")
+LIB = os.path.join(ROOT, "gqa_attention_grok_amd", "libgrokattn.so")
+
+EINVAL, ENOMEM, ERANGE, EHIP = -22, -12, -34, -5
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation rejects first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"GROK_API\s+[\w\s\*]*?\b(grok_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from gqa_attention_grok_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) == 10, syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    vals = dict(re.findall(r"#define (GROK_\w+) \(?(-?\d+)\)?", text))
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_b", os.path.join(ROOT, "gqa_attention_grok_amd", "__init__.py"))
+    src = open(spec.origin).read()
+    for name in ("GROK_BF16", "GROK_F32", "GROK_EINVAL", "GROK_ERANGE", "GROK_ENOMEM", "GROK_EHIP"):
+        assert name in vals
+        assert re.search(name, src), name
+    assert int(vals["GROK_EINVAL"]) == EINVAL and int(vals["GROK_ERANGE"]) == ERANGE
+
+
+def _c(lib, name, *args, restype=ctypes.c_int):
+    f = getattr(lib, name)
+    f.restype = restype
+    return f(*args)
+
+
+def _err(lib):
+    f = lib.grok_last_error
+    f.restype = ctypes.c_char_p
+    return f().decode()
+
+
+def test_version_and_status_strings(lib):
+    assert _c(lib, "grok_abi_version") == 1
+    f = lib.grok_status_string
+    f.restype = ctypes.c_char_p
+    assert f(EINVAL) == b"invalid argument"
+    assert f(ERANGE) == b"cache position out of range"
+
+
+i, i64, fl = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+
+
+def test_rmsnorm_validation(lib):
+    assert _c(lib, "grok_rmsnorm", None, None, None, FAKE, i64(4), i(8), fl(1e-5), i(0), None) == EINVAL
+    assert "null" in _err(lib)
+    assert _c(lib, "grok_rmsnorm", FAKE, None, None, FAKE, i64(4), i(0), fl(1e-5), i(0), None) == EINVAL
+    assert _c(lib, "grok_rmsnorm", FAKE, None, None, FAKE, i64(4), i(8), fl(-1.0), i(0), None) == EINVAL
+    assert _c(lib, "grok_rmsnorm", FAKE, None, None, FAKE, i64(4), i(8), fl(1e-5), i(7), None) == EINVAL
+    # zero rows: nothing to do, success without touching the pointers
+    assert _c(lib, "grok_rmsnorm", None, None, None, None, i64(0), i(8), fl(1e-5), i(0), None) == 0
+
+
+def test_linear_validation(lib):
+    ok = (FAKE, FAKE, FAKE, FAKE)
+    assert _c(lib, "grok_linear_int8", *ok, i64(4), i(12), i(16), None) == EINVAL  # K % 8
+    assert _c(lib, "grok_linear_int8", *ok, i64(4), i(16), i(12), None) == EINVAL  # N % 8
+    assert _c(lib, "grok_linear_int8", FAKE, None, FAKE, FAKE, i64(4), i(16), i(16), None) == EINVAL
+    assert _c(lib, "grok_linear_int8", ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, i64(4), i(16), i(16), None) == EINVAL
+    assert _c(lib, "grok_linear_int8", None, None, None, None, i64(0), i(16), i(16), None) == 0
+
+
+def test_rope_validation(lib):
+    assert _c(lib, "grok_rope", FAKE, i(1), i(2), i(3), i(5), None, fl(1e4), i(0), None) == EINVAL  # odd D
+    assert _c(lib, "grok_rope", FAKE, i(1), i(2), i(3), i(514), None, fl(1e4), i(0), None) == EINVAL
+    assert _c(lib, "grok_rope", FAKE, i(1), i(2), i(3), i(8), None, fl(0.0), i(0), None) == EINVAL
+    assert _c(lib, "grok_rope", None, i(1), i(2), i(3), i(8), None, fl(1e4), i(0), None) == EINVAL
+    assert _c(lib, "grok_rope", None, i(0), i(2), i(3), i(8), None, fl(1e4), i(0), None) == 0
+
+
+def test_kv_append_validation(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None]
+    def call(B=1, T=1, Tmax=16, Hq=6, Hkv=1, D=128, base=1e4, a=args):
+        return _c(lib, "grok_kv_append", *a, i(B), i(T), i(Tmax), i(Hq), i(Hkv), i(D), fl(base), None)
+    assert call(T=17) == EINVAL          # more new tokens than the cache holds
+    assert call(Hq=7, Hkv=2) == EINVAL   # Hq % Hkv
+    assert call(D=24) == EINVAL          # D % 16
+    assert call(B=0) == EINVAL
+    bad = list(args)
+    bad[5] = None                        # step
+    assert call(a=bad) == EINVAL
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(0x10002)    # misaligned cache
+    assert call(a=bad) == EINVAL
+
+
+def test_prefill_validation(lib):
+    def call(T=16, kv_rows=16, Hq=6, Hkv=1, D=32, mult=0.17, cap=30.0, dtype=1, kv=None, q=FAKE):
+        return _c(lib, "grok_attn_prefill", q, FAKE, FAKE, i64(kv_rows), kv, FAKE, i(1), i(T), i(Hq),
+                  i(Hkv), i(D), fl(mult), fl(cap), i(dtype), None)
+    assert call(Hq=7, Hkv=2) == EINVAL
+    assert call(kv_rows=8) == EINVAL
+    assert call(D=12) == EINVAL
+    assert call(D=264) == EINVAL
+    assert call(cap=0.0) == EINVAL
+    assert call(cap=50.0) == EINVAL
+    assert call(mult=float("inf")) == EINVAL
+    assert call(dtype=3) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(D=128, dtype=0, q=ctypes.c_void_p(0x10004)) == EINVAL  # MFMA path needs 16-B alignment
+
+
+def test_decode_validation_and_workspace(lib):
+    ws = lib.grok_attn_decode_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    n = ws(i(1), i(8192), i(48), i(8), i(128))
+    # 64 splits x 8 KV heads x 6 heads x (128 + 1) floats
+    assert n == 64 * 8 * 6 * 129 * 4
+    assert ws(i(1), i(8192), i(48), i(8), i(64)) == 0
+    assert ws(i(1), i(8192), i(47), i(8), i(128)) == 0
+
+    def call(B=1, Tmax=8192, Hq=48, Hkv=8, D=128, nbytes=n, cap=30.0):
+        return _c(lib, "grok_attn_decode", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_size_t(nbytes), None,
+                  i(B), i(Tmax), i(Hq), i(Hkv), i(D), fl(0.088), fl(cap), None)
+    assert call(nbytes=n - 4) == ENOMEM
+    assert call(D=64) == EINVAL
+    assert call(Hq=44) == EINVAL
+    assert call(Hq=136, Hkv=8) == EINVAL  # 17 heads per KV head
+    assert call(cap=-1.0) == EINVAL

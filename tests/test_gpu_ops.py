@@ -1,0 +1,330 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles and ragged tails,
+plus the edge cases (empty, ragged, degenerate masks, out-of-range positions)."""
+import math
+
+import numpy as np
+import pytest
+
+import gqa_inputs as gi
+import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gqa_attention_grok_amd as grok
+    import gpu_util
+    return grok, gpu_util, torch
+
+
+# --------------------------------------------------------------------------
+# RMSNorm
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,d,use_gamma,use_res,dtype", [
+    (37, 6144, False, False, "bf16"),
+    (37, 6144, True, True, "bf16"),
+    (5, 100, True, True, "bf16"),      # row not a multiple of the vector width
+    (2, 8200, False, True, "bf16"),    # row wider than the register-resident path
+    (9, 64, True, False, "f32"),
+    (3, 6, False, True, "f32"),
+])
+def test_rmsnorm(G, rows, d, use_gamma, use_res, dtype):
+    grok, U, torch = G
+    g = gi.rng(10 + d)
+    if dtype == "bf16":
+        xb, rb = gi.normal_bf16(g, (rows, d)), gi.normal_bf16(g, (rows, d))
+        x, r = U.dev_bf16(xb), U.dev_bf16(rb)
+        x64, r64 = orc.bf16_bits_to_f64(xb), orc.bf16_bits_to_f64(rb)
+    else:
+        x64 = gi.normal_f32(g, (rows, d)) * 3
+        r64 = gi.normal_f32(g, (rows, d))
+        x, r = U.dev(x64), U.dev(r64)
+        x64, r64 = x64.astype(np.float64), r64.astype(np.float64)
+    gam = g.uniform(0.5, 1.5, d).astype(np.float32) if use_gamma else None
+    y = torch.empty_like(x)
+    grok.grok_rmsnorm(x, y, gamma=U.dev(gam) if use_gamma else None, residual=r if use_res else None)
+    ref = orc.rmsnorm(x64, gam, 1e-5, residual=r64 if use_res else None, out=dtype)
+    if dtype == "bf16":
+        U.assert_bf16_close(U.host(y), ref, "rmsnorm")
+    else:
+        U.assert_f32_close(U.host(y), ref, "rmsnorm")
+
+
+def test_rmsnorm_in_place_and_empty(G):
+    grok, U, torch = G
+    xb = gi.normal_bf16(gi.rng(3), (4, 6144))
+    x = U.dev_bf16(xb)
+    grok.grok_rmsnorm(x, x)
+    U.assert_bf16_close(U.host(x), orc.rmsnorm(orc.bf16_bits_to_f64(xb), out="bf16"), "in place")
+    e = torch.empty((0, 6144), dtype=torch.bfloat16, device="cuda")
+    grok.grok_rmsnorm(e, e)
+
+
+# --------------------------------------------------------------------------
+# int8 Linear
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N,distinct", [
+    (300, 6144, 1024, True),   # ragged rows, several K steps
+    (130, 40, 24, True),       # K tail inside one step, partial channel tile
+    (1, 8, 8, False),
+    (257, 512, 6144, True),
+])
+def test_linear_int8(G, M, K, N, distinct):
+    grok, U, torch = G
+    g = gi.rng(M + K + N)
+    xb = gi.normal_bf16(g, (M, K))
+    w = gi.int8_uniform(g, (K, N))
+    s = (0.02 / 127 * g.uniform(0.5, 1.5, N) if distinct else np.full(N, 0.02 / 127)).astype(np.float32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    grok.grok_linear_int8(U.dev_bf16(xb), U.dev(w), U.dev(s), y)
+    ref = orc.linear_int8(orc.bf16_bits_to_f64(xb), w, s, out="bf16")
+    U.assert_bf16_close(U.host(y), ref, "linear_int8")
+
+
+def test_linear_int8_scale_axis_and_empty(G):
+    grok, U, torch = G
+    K, N = 64, 16
+    w = np.zeros((K, N), np.int8)
+    w[np.arange(N) * 3, np.arange(N)] = 127  # channel n reads input 3n
+    s = (np.arange(1, N + 1) / 127).astype(np.float32)
+    xb = gi.normal_bf16(gi.rng(4), (5, K))
+    y = torch.empty((5, N), dtype=torch.bfloat16, device="cuda")
+    grok.grok_linear_int8(U.dev_bf16(xb), U.dev(w), U.dev(s), y)
+    x64 = orc.bf16_bits_to_f64(xb)
+    ref = orc.round_bf16(x64[:, np.arange(N) * 3] * 127 * s.astype(np.float64))
+    np.testing.assert_array_equal(U.host(y), ref)
+    e = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    grok.grok_linear_int8(e, U.dev(w), U.dev(s), torch.empty((0, N), dtype=torch.bfloat16, device="cuda"))
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,dtype,offsets", [
+    ((2, 37, 5, 128), "bf16", [0, 8000]),
+    ((1, 16, 6, 32), "f32", None),
+    ((3, 4, 2, 6), "f32", [5, 0, 8191]),   # pair count not a multiple of the vector width
+    ((1, 3, 48, 128), "bf16", [8189]),
+])
+def test_rope(G, shape, dtype, offsets):
+    grok, U, torch = G
+    g = gi.rng(sum(shape))
+    B, T = shape[:2]
+    if dtype == "bf16":
+        xb = gi.normal_bf16(g, shape)
+        x, x64 = U.dev_bf16(xb), orc.bf16_bits_to_f64(xb)
+    else:
+        xf = gi.normal_f32(g, shape)
+        x, x64 = U.dev(xf), xf.astype(np.float64)
+    off = np.zeros(B, np.int32) if offsets is None else np.asarray(offsets, np.int32)
+    grok.grok_rope(x, None if offsets is None else U.dev(off))
+    pos = off[:, None] + np.arange(T)[None, :]
+    ref = orc.rope(x64, pos, out=dtype)
+    if dtype == "bf16":
+        U.assert_bf16_close(U.host(x), ref, "rope")
+    else:
+        U.assert_f32_close(U.host(x), ref, "rope")
+    if offsets is None or 0 in list(off):
+        b0 = int(np.argmax(off == 0))
+        np.testing.assert_array_equal(U.host(x)[b0, 0], x64[b0, 0])  # position 0: identity
+
+
+# --------------------------------------------------------------------------
+# KV append
+# --------------------------------------------------------------------------
+def test_kv_append_rope_and_bit_exact_slots(G):
+    grok, U, torch = G
+    g = gi.rng(77)
+    B, T, Tmax, Hq, Hkv, D = 3, 2, 64, 12, 2, 128
+    kc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    vc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    kn, vn = gi.normal_bf16(g, (B, T, Hkv, D)), gi.normal_bf16(g, (B, T, Hkv, D))
+    qb = gi.normal_bf16(g, (B, T, Hq, D))
+    step = np.array([0, 30, 62], np.int32)
+    kc, vc, q = U.dev_bf16(kc0), U.dev_bf16(vc0), U.dev_bf16(qb)
+    new_step = torch.zeros(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grok.grok_kv_append(kc, vc, U.dev_bf16(kn), U.dev_bf16(vn), U.dev(step), q_inout=q,
+                        new_step=new_step, status=status)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    np.testing.assert_array_equal(new_step.cpu().numpy(), step + T)
+    # reference rotation of the same values by the standalone RoPE entry point
+    kr, qr = U.dev_bf16(kn), U.dev_bf16(qb)
+    grok.grok_rope(kr, U.dev(step))
+    grok.grok_rope(qr, U.dev(step))
+    kcb, vcb = U.bits(kc), U.bits(vc)
+    pos = step[:, None] + np.arange(T)[None]
+    ref_k = orc.rope(orc.bf16_bits_to_f64(kn), pos, out="bf16")
+    for b in range(B):
+        sl = slice(step[b], step[b] + T)
+        np.testing.assert_array_equal(vcb[b, sl], vn[b])             # V: bit copy
+        np.testing.assert_array_equal(kcb[b, sl], U.bits(kr)[b])     # K: = grok_rope bits
+        keep = np.ones(Tmax, bool)
+        keep[sl] = False
+        np.testing.assert_array_equal(kcb[b, keep], kc0[b, keep])    # other slots untouched
+        np.testing.assert_array_equal(vcb[b, keep], vc0[b, keep])
+    U.assert_bf16_close(orc.bf16_bits_to_f64(np.stack([kcb[b, step[b]:step[b] + T] for b in range(B)])),
+                        ref_k, "roped k")
+    np.testing.assert_array_equal(U.bits(q), U.bits(qr))
+    U.assert_bf16_close(U.host(q), orc.rope(orc.bf16_bits_to_f64(qb), pos, out="bf16"), "roped q")
+
+
+def test_kv_append_out_of_range_and_no_rope(G):
+    grok, U, torch = G
+    g = gi.rng(78)
+    B, T, Tmax, Hkv, D = 2, 2, 16, 1, 32
+    kc0, vc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D)), gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    kn, vn = gi.normal_bf16(g, (B, T, Hkv, D)), gi.normal_bf16(g, (B, T, Hkv, D))
+    step = np.array([15, 4], np.int32)  # sequence 0 would overflow the cache
+    kc, vc = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    ns = torch.zeros(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grok.grok_kv_append(kc, vc, U.dev_bf16(kn), U.dev_bf16(vn), U.dev(step), new_step=ns,
+                        status=status, rope_base=0.0)
+    torch.cuda.synchronize()
+    assert status.item() == grok.GROK_ERANGE
+    np.testing.assert_array_equal(ns.cpu().numpy(), [15, 6])
+    kcb, vcb = U.bits(kc), U.bits(vc)
+    np.testing.assert_array_equal(kcb[0], kc0[0])
+    np.testing.assert_array_equal(vcb[0], vc0[0])
+    np.testing.assert_array_equal(kcb[1, 4:6], kn[1])  # no RoPE: plain copy
+    np.testing.assert_array_equal(vcb[1, 4:6], vn[1])
+
+
+# --------------------------------------------------------------------------
+# Prefill
+# --------------------------------------------------------------------------
+def _prefill_case(G, B, T, Hq, Hkv, D, dtype, mult, pad=None, kv_rows=None, seed=0):
+    grok, U, torch = G
+    p = gi.make_prefill_inputs(B, T, Hq, Hkv, D, seed=seed, dtype=dtype)
+    to_dev = U.dev_bf16 if dtype == "bf16" else U.dev
+    to64 = orc.bf16_bits_to_f64 if dtype == "bf16" else (lambda a: a.astype(np.float64))
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    if kv_rows is not None:  # K/V read in place from a longer buffer (cache stride)
+        kk = torch.zeros((B, kv_rows, Hkv, D), dtype=q.dtype, device="cuda")
+        vv = torch.zeros_like(kk)
+        kk[:, :T] = k
+        vv[:, :T] = v
+        kk[:, T:] = 7.0  # finite garbage beyond T is never read
+        vv[:, T:] = 7.0
+        k, v = kk, vv
+    kv = None if pad is None else U.dev(pad)
+    out = torch.empty((B, T, Hq * D), dtype=q.dtype, device="cuda")
+    grok.grok_attn_prefill(q, k, v, out, mult, 30.0, key_valid=kv)
+    pos = np.broadcast_to(np.arange(T), (B, T))
+    mask = orc.attention_mask(pos, T, key_valid=pad)
+    ref = orc.attention(to64(p["q"]), to64(p["k"]), to64(p["v"]), mask, mult, 30.0, out=dtype)
+    got = U.host(out)
+    if dtype == "bf16":
+        U.assert_bf16_close(got, ref, f"prefill B={B} T={T} Hq={Hq} Hkv={Hkv}")
+    else:
+        U.assert_f32_close(got, ref, f"prefill B={B} T={T}")
+    return got, p
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,scale", [
+    (2, 300, 48, 8, 4.0),   # Grok grouping, several query/key tiles, ragged tail
+    (1, 64, 48, 8, 1.0),
+    (1, 64, 8, 8, 1.0),     # MHA
+    (1, 50, 12, 1, 1.0),    # one KV head, 12 query heads
+    (1, 40, 16, 2, 2.0),    # 8 query heads per KV head
+    (2, 33, 10, 2, 1.0),    # 5 per KV head
+    (1, 1, 48, 8, 1.0),     # a single token
+])
+def test_prefill_mfma(G, B, T, Hq, Hkv, scale):
+    _prefill_case(G, B, T, Hq, Hkv, 128, "bf16", scale / math.sqrt(128), seed=B * T + Hq)
+
+
+def test_prefill_mfma_padding_and_fully_masked_rows(G):
+    B, T = 2, 77
+    pad = np.ones((B, T), np.uint8)
+    pad[0, :5] = 0          # rows 0..4 of sequence 0 see no valid key
+    pad[0, 40:45] = 0
+    pad[1, ::3] = 0
+    U = G[1]
+    got, p = _prefill_case(G, B, T, 48, 8, 128, "bf16", 1 / math.sqrt(128), pad=pad, seed=5)
+    vmean = orc.bf16_bits_to_f64(p["v"])[0].mean(0)  # [Hkv, D] over all T keys
+    for t in range(5):
+        row = got[0, t].reshape(48, 128)
+        for h in range(48):
+            U.assert_bf16_close(row[h], orc.round_bf16(vmean[h // 6]), "fully masked row")
+
+
+def test_prefill_mfma_cache_stride(G):
+    _prefill_case(G, 2, 70, 48, 8, 128, "bf16", 1 / math.sqrt(128), kv_rows=100, seed=9)
+
+
+def test_prefill_row0_equals_v0_bit_exact(G):
+    grok, U, torch = G
+    got, p = _prefill_case(G, 1, 96, 48, 8, 128, "bf16", 4 / math.sqrt(128), seed=11)
+    v0 = orc.bf16_bits_to_f64(p["v"])[0, 0]  # [Hkv, D]
+    for h in range(48):
+        np.testing.assert_array_equal(got[0, 0, h * 128:(h + 1) * 128], v0[h // 6])
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,dtype,padded", [
+    (1, 16, 6, 1, 32, "f32", False),
+    (2, 45, 12, 2, 64, "bf16", True),
+    (1, 20, 4, 2, 128, "f32", True),
+    (1, 9, 3, 3, 256, "bf16", False),
+])
+def test_prefill_generic(G, B, T, Hq, Hkv, D, dtype, padded):
+    pad = None
+    if padded:
+        pad = np.ones((B, T), np.uint8)
+        pad[0, 0] = 0
+        pad[-1, T // 2] = 0
+    _prefill_case(G, B, T, Hq, Hkv, D, dtype, 1 / math.sqrt(D), pad=pad, seed=T + D)
+
+
+# --------------------------------------------------------------------------
+# Decode
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("Hq,Hkv,lens,Tmax", [
+    (48, 8, [1, 127, 128, 129, 1024], 1024),
+    (16, 1, [33, 300], 512),
+    (8, 8, [5, 256], 256),
+])
+def test_decode(G, Hq, Hkv, lens, Tmax):
+    grok, U, torch = G
+    B, D = len(lens), 128
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=Tmax + Hq, lengths=lens)
+    kv_len = np.asarray(lens, np.int32)
+    q = U.dev_bf16(p["q"])
+    out = torch.empty((B, 1, Hq * D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8,
+                     device="cuda")
+    mult = 1 / math.sqrt(D)
+    grok.grok_attn_decode(q, U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"]), U.dev(kv_len), out,
+                          ws, mult)
+    mask = orc.attention_mask((kv_len - 1)[:, None], Tmax, kv_len=kv_len)
+    ref = orc.attention(orc.bf16_bits_to_f64(p["q"]), orc.bf16_bits_to_f64(p["k_cache"]),
+                        orc.bf16_bits_to_f64(p["v_cache"]), mask, mult, 30.0, out="bf16")
+    U.assert_bf16_close(U.host(out), ref, "decode")
+    assert U.rel_l2(U.host(out), ref) < 1e-2
+
+
+def test_decode_bad_lengths_give_zero_rows_and_status(G):
+    grok, U, torch = G
+    B, Tmax, Hq, Hkv, D = 3, 256, 48, 8, 128
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=3, lengths=[10, 10, 10])
+    kv_len = np.array([0, 100, Tmax + 1], np.int32)
+    out = torch.full((B, 1, Hq * D), 5.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8,
+                     device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grok.grok_attn_decode(U.dev_bf16(p["q"]), U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"]),
+                          U.dev(kv_len), out, ws, 1 / math.sqrt(D), status=status)
+    torch.cuda.synchronize()
+    assert status.item() == grok.GROK_ERANGE
+    got = U.host(out)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    mask = orc.attention_mask(np.array([[99]]), Tmax, kv_len=np.array([100]))
+    ref = orc.attention(orc.bf16_bits_to_f64(p["q"][1:2]), orc.bf16_bits_to_f64(p["k_cache"][1:2]),
+                        orc.bf16_bits_to_f64(p["v_cache"][1:2]), mask, 1 / math.sqrt(D), out="bf16")
+    U.assert_bf16_close(got[1:2], ref, "valid row next to bad ones")

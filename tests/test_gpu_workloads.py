@@ -1,0 +1,155 @@
+"""The five named workloads at full size, run through the same step objects the
+benchmark times, checked against the fp64 oracle: in full where the oracle is
+cheap (tiny prefill, both decodes), on sampled output rows that the oracle
+computes one by one otherwise (8k prefill, full sub-layer)."""
+import math
+
+import numpy as np
+import pytest
+
+import gqa_inputs as gi
+import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gqa_attention_grok_amd as grok
+    import gqa_attention_grok_amd.pipeline as pipe
+    import gpu_util
+    return grok, pipe, gpu_util, torch
+
+
+def test_c1_tiny_prefill_f32(G):
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS["c1_tiny_prefill_f32"]
+    p = gi.make_workload(w.name)
+    step = pipe.PrefillStep(U.dev(p["q"]), U.dev(p["k"]), U.dev(p["v"]), w.attn_mult, w.softcap)
+    out = U.host(step())
+    pos = np.arange(w.T)[None]
+    q = orc.rope(p["q"].astype(np.float64), pos, out="f32")
+    k = orc.rope(p["k"].astype(np.float64), pos, out="f32")
+    ref = orc.attention(q, k, p["v"].astype(np.float64), orc.attention_mask(pos, w.T), w.attn_mult,
+                        w.softcap, out="f32")
+    err = U.assert_f32_close(out, ref, "c1")
+    print(f"c1 max abs err {err:.2e}")
+
+
+def _decode_check(G, name):
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS[name]
+    p = gi.make_workload(name)
+    kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    step = pipe.DecodeStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                           U.dev(p["step"]), w.attn_mult, w.softcap)
+    out = U.host(step())
+    torch.cuda.synchronize()
+    assert step.status.item() == 0
+    np.testing.assert_array_equal(step.kv_len.cpu().numpy(), p["kv_len"])
+    B = w.B
+    # oracle: RoPE q and k_new at step[b], append, attend [0, step+1)
+    q = orc.bf16_bits_to_f64(p["q"])
+    kn = orc.bf16_bits_to_f64(p["k_new"])
+    vn = orc.bf16_bits_to_f64(p["v_new"])
+    pos = p["step"].reshape(B, 1)
+    qr = orc.rope(q, pos, out="bf16")
+    kr = orc.rope(kn, pos, out="bf16")
+    kcb, vcb = U.bits(kc), U.bits(vc)
+    errs = []
+    for b in range(B):
+        s = int(p["step"][b])
+        # cache: V slot bit copy, K slot roped, every other slot untouched
+        np.testing.assert_array_equal(vcb[b, s], p["v_new"][b, 0])
+        U.assert_bf16_close(orc.bf16_bits_to_f64(kcb[b, s]), kr[b, 0], "appended k")
+        np.testing.assert_array_equal(kcb[b, :s], p["k_cache"][b, :s])
+        np.testing.assert_array_equal(kcb[b, s + 1:], p["k_cache"][b, s + 1:])
+        np.testing.assert_array_equal(vcb[b, :s], p["v_cache"][b, :s])
+        np.testing.assert_array_equal(vcb[b, s + 1:], p["v_cache"][b, s + 1:])
+        L = s + 1
+        k64 = orc.bf16_bits_to_f64(p["k_cache"][b:b + 1, :L])
+        v64 = orc.bf16_bits_to_f64(p["v_cache"][b:b + 1, :L])
+        k64[0, s] = kr[b, 0]
+        v64[0, s] = vn[b, 0]
+        ref = orc.attention(qr[b:b + 1], k64, v64, np.ones((1, 1, L), bool), w.attn_mult, w.softcap,
+                            out="bf16")
+        errs.append(U.assert_bf16_close(out[b:b + 1], ref, f"{name} b={b}"))
+        # stricter self-check: the outputs are small averages, so also bound the
+        # error relative to the output scale
+        assert np.max(np.abs(out[b:b + 1] - ref)) <= 2e-2 * np.max(np.abs(ref))
+        assert U.rel_l2(out[b:b + 1], ref) < 1e-2
+    print(f"{name} max abs err {max(errs):.2e}")
+
+
+def test_c2_decode_b1(G):
+    _decode_check(G, "c2_decode_b1")
+
+
+def test_c4_decode_ragged_b32(G):
+    _decode_check(G, "c4_decode_ragged_b32")
+
+
+def test_c3_prefill_t8192_sampled(G):
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS["c3_prefill_t8192"]
+    p = gi.make_workload(w.name)
+    step = pipe.PrefillStep(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), w.attn_mult,
+                            w.softcap)
+    out = step()
+    torch.cuda.synchronize()
+    T, Hq, Hkv, D = w.T, w.Hq, w.Hkv, w.D
+    pos = np.arange(T)[None]
+    k = orc.rope(orc.bf16_bits_to_f64(p["k"]), pos, out="bf16")
+    v = orc.bf16_bits_to_f64(p["v"])
+    g = gi.rng(31337)
+    rows = [0, 1, 31, 32, 4095, 8190, 8191] + list(g.integers(0, T, 25))
+    got = U.host(out[0, rows]).reshape(len(rows), Hq, D)
+    # row 0 attends only to key 0: its weight is exactly one
+    for h in range(Hq):
+        np.testing.assert_array_equal(got[0, h], v[0, 0, h // (Hq // Hkv)])
+    errs = []
+    for r, t in enumerate(rows):
+        qt = orc.rope(orc.bf16_bits_to_f64(p["q"][:, t:t + 1]), np.array([[t]]), out="bf16")
+        mask_row = np.arange(T) <= t
+        for h in range(Hq):
+            ref = orc.round_bf16(orc.attention_rows(qt, k, v[None] if v.ndim == 3 else v, 0, 0, h,
+                                                    mask_row, w.attn_mult, w.softcap))
+            errs.append(U.assert_bf16_close(got[r, h], ref, f"c3 t={t} h={h}"))
+    print(f"c3 sampled {len(rows)} rows x {Hq} heads, max abs err {max(errs):.2e}")
+
+
+def test_c5_sublayer_sampled(G):
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS["c5_sublayer_b4_t2048"]
+    p = gi.make_workload(w.name)
+    dv = {k: (U.dev_bf16(v) if k == "x" else U.dev(v)) for k, v in p.items()}
+    step = pipe.SublayerStep(dv["x"], dv["wq"], dv["sq"], dv["wk"], dv["sk"], dv["wv"], dv["sv"],
+                             dv["wo"], dv["so"], w.Hq, w.Hkv, w.D, w.attn_mult, w.softcap, w.eps)
+    y = step()
+    torch.cuda.synchronize()
+    B, T, d, Hq, Hkv, D = w.B, w.T, w.d_model, w.Hq, w.Hkv, w.D
+    x = orc.bf16_bits_to_f64(p["x"])
+    n = orc.rmsnorm(x, None, w.eps, out="bf16")
+    U.assert_bf16_close(U.host(step.n), n, "c5 pre-norm")
+    g = gi.rng(4242)
+    errs = []
+    for b in (0, 3):
+        kb = orc.linear_int8(n[b], p["wk"], p["sk"], out="bf16").reshape(1, T, Hkv, D)
+        vb = orc.linear_int8(n[b], p["wv"], p["sv"], out="bf16").reshape(1, T, Hkv, D)
+        U.assert_bf16_close(U.host(step.v[b:b + 1]), vb, "c5 v projection")
+        kb = orc.rope(kb, np.arange(T)[None], out="bf16")
+        U.assert_bf16_close(U.host(step.k[b:b + 1]), kb, "c5 roped k")
+        for t in [0, 1, 2047] + list(g.integers(0, T, 5)):
+            qt = orc.linear_int8(n[b, t], p["wq"], p["sq"], out="bf16").reshape(1, 1, Hq, D)
+            qt = orc.rope(qt, np.array([[t]]), out="bf16")
+            mask_row = np.arange(T) <= t
+            a = np.concatenate([orc.attention_rows(qt, kb, vb, 0, 0, h, mask_row, w.attn_mult, w.softcap)
+                                for h in range(Hq)])
+            a = orc.round_bf16(a)
+            U.assert_bf16_close(U.host(step.attn[b, t]), a, f"c5 attention b={b} t={t}")
+            o = orc.linear_int8(a, p["wo"], p["so"], out="bf16")
+            yt = orc.rmsnorm(o[None], None, w.eps, residual=x[b, t][None], out="bf16")[0]
+            errs.append(U.assert_bf16_close(U.host(y[b, t]), yt, f"c5 output b={b} t={t}"))
+    print(f"c5 sampled rows, max abs err {max(errs):.2e}")
