@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="", help="comma list of c2,c3,c4,c5 (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -65,18 +67,32 @@ def traffic_for(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def time_steps(torch, fn, steps, warmup, inner=None):
-    """Warm up, then time `steps` calls of fn() between two synchronisations.
-    `inner(i)` (optional) returns (start_event, end_event) pairs recorded around
-    the dominant kernel inside step i."""
-    for _ in range(warmup):
-        fn(-1)
+def time_replays(torch, graphs, steps, warmup):
+    """Warm up, then time `steps` replays (cycling over `graphs`) between two
+    device synchronisations; returns seconds per step."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        fn(i)
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def time_kernel(torch, fn, reps):
+    """Mean duration of the kernel(s) `fn` launches, from HIP events recorded on
+    the stream they are launched on (torch's current stream)."""
+    fn(0)
+    ev = []
+    for i in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
 def bench_prefill(torch, grok, pipe, U, gi, steps, warmup):
@@ -86,21 +102,9 @@ def bench_prefill(torch, grok, pipe, U, gi, steps, warmup):
                           w.softcap)
     del p
     flop = 4 * w.D * w.Hq * w.B * w.T * (w.T + 1) // 2
-    ev = []
-
-    def step(i):
-        st.rope()
-        if i >= 0:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            st.attend()
-            e.record()
-            ev.append((s, e))
-        else:
-            st.attend()
-
-    sec = time_steps(torch, step, steps, warmup)
-    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    g = pipe.capture(st)
+    sec = time_replays(torch, [g], steps, warmup)
+    kern_ms = time_kernel(torch, lambda i: st.attend(), max(steps, 5))
     return {
         "workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12, "unit": "TFLOP/s",
         "flop_per_step": flop, "kernel": "prefill_mfma_kernel", "kernel_ms": kern_ms,
@@ -124,23 +128,15 @@ def bench_decode(torch, grok, pipe, U, gi, name, steps, warmup, replicas):
     kv_bytes = int(L.sum()) * Hkv * D * 2 * 2
     io_bytes = w.B * (Hq * D * 2 + 2 * Hkv * D * 2 + Hq * D * 2)
     nbytes = kv_bytes + io_bytes
-    ev = []
+    graphs = [pipe.capture(s_) for s_ in steps_obj]
+    sec = time_replays(torch, graphs, steps, warmup)
 
-    def step(i):
-        s_ = steps_obj[(i if i >= 0 else 0) % len(steps_obj)]
-        grok.grok_kv_append(s_.k_cache, s_.v_cache, s_.k_new, s_.v_new, s_.step, q_inout=s_.q,
-                            new_step=s_.kv_len, status=s_.status, rope_base=s_.rope_base)
-        if i >= 0:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+    def attend(i):
+        s_ = steps_obj[i % len(steps_obj)]
         grok.grok_attn_decode(s_.q, s_.k_cache, s_.v_cache, s_.kv_len, s_.out, s_.workspace,
                               s_.attn_mult, s_.softcap, status=s_.status)
-        if i >= 0:
-            b.record()
-            ev.append((a, b))
 
-    sec = time_steps(torch, step, steps, warmup)
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern_ms = time_kernel(torch, attend, max(steps, 2 * len(steps_obj)))
     return {
         "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",
         "bytes_per_step": nbytes, "kernel": "decode_split_kernel+decode_combine_kernel",
@@ -161,7 +157,7 @@ def bench_sublayer(torch, grok, pipe, U, gi, steps, warmup):
     proj = 2 * M * d * (w.Hq * w.D + 2 * w.Hkv * w.D) + 2 * M * (w.Hq * w.D) * d
     attn = 4 * w.D * w.Hq * w.B * w.T * (w.T + 1) // 2
     flop = proj + attn
-    sec = time_steps(torch, lambda i: st(), steps, warmup)
+    sec = time_replays(torch, [pipe.capture(st)], steps, warmup)
     return {"workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12,
             "unit": "TFLOP/s", "flop_per_step": flop}
 
@@ -207,6 +203,15 @@ def main():
 
     only = set(args.only.split(",")) if args.only else {"c2", "c3", "c4", "c5"}
     res = {}
+    if args.copy_calibration:
+        # a plain copy of known size: reads and writes exactly 256 MiB
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("# copy calibration done: 268435456 bytes read and written", file=sys.stderr, flush=True)
     if "c3" in only:
         res["c3"] = bench_prefill(torch, grok, pipe, U, gi, args.steps, args.warmup)
         print(f"# c3 done: {res['c3']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)

@@ -9,15 +9,19 @@
 //   16 consecutive positions of one query head. The 12 blocks are Gc heads of
 //   one KV group x (12/Gc) position blocks, so every K/V tile staged in LDS is
 //   used by all those heads (for Grok-1's 6:1 grouping: 6 heads x 32 positions).
-//   Each wave owns 3 row blocks and walks the causal key range in tiles of 32.
+//   Each wave owns 3 row blocks and walks the causal key range in tiles of 64
+//   keys, double-buffered in LDS (one barrier per tile).
 //
 // MFMA formulation (v_mfma_f32_16x16x32_bf16), transposed so that each lane
 // always holds data of query row (lane % 16):
 //   S^T[key, row]  = K[key, :] . Q[row, :]^T          A = K (LDS), B = Q (regs)
 //   O^T[d, row]   += V^T[d, key] . P^T[key, row]      A = V^T (LDS), B = P (regs)
 //   The K rows feeding S^T are permuted so that the S^T accumulator of lane l
-//   holds keys 8*(l/16) .. 8*(l/16)+7 for its row -- exactly the B-operand
-//   layout P needs for the P.V product, so P never leaves registers.
+//   holds keys 8*(l/16) .. 8*(l/16)+7 of a 32-key half for its row -- exactly
+//   the B-operand layout P needs for the P.V product, so P never leaves
+//   registers. The permutation is applied when K is stored into LDS, so the
+//   fragment reads walk consecutive rows. V is transposed while it is stored
+//   (4 keys per 8-byte LDS write).
 //
 // Softmax without a running max: after the softcap every unmasked logit lies in
 // [-cap, cap], so p = exp(c - cap) is in [exp(-2cap), 1] -- no overflow, and no
@@ -38,9 +42,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRB = 3;             // row blocks per wave
 constexpr int kRowBlocks = kWaves * kRB;
-constexpr int kBN = 32;            // keys per tile
-constexpr int kKRow = kD + 8;      // padded LDS row of K (bf16 elements)
-constexpr int kVRow = kBN + 8;     // padded LDS row of V^T (bf16 elements)
+constexpr int kBN = 64;            // keys per tile (two halves of 32 per MFMA step)
+constexpr int kKRow = kD + 8;      // padded LDS row of K: 272 B, 17 16-byte slots
+constexpr int kVRow = kBN + 8;     // padded LDS row of V^T: 144 B, 9 16-byte slots
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -50,6 +54,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   f32x2 f = {a, b};
   bf16x2 h = __builtin_convertvector(f, bf16x2);
   return __builtin_bit_cast(uint32_t, h);
+}
+
+// LDS row of key j (0..63) in a K tile. The S^T MFMA of half h, key block kb
+// reads, in lane order, the keys 32h + 8*(r/4) + 4*kb + r%4 (r = lane % 16);
+// storing them at consecutive rows 32h + 16*kb + r makes those 16-byte reads
+// hit distinct bank groups.
+__device__ __forceinline__ int k_lds_row(int j) {
+  const int h = j >> 5, r = j & 31;
+  return 32 * h + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
 struct PrefillArgs {
@@ -115,120 +128,167 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   }
 
   f32x4 oacc[kRB][8];
+  float lsum[kRB];  // this lane's part of each row's weight sum
 #pragma unroll
-  for (int i = 0; i < kRB; ++i)
+  for (int i = 0; i < kRB; ++i) {
+    lsum[i] = 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db) oacc[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum[kRB] = {0.f, 0.f, 0.f};
+  }
 
-  // Tile loader: K chunks (2 per thread), V key pairs (2 rows x 16 B per thread).
+  // Tile staging. K: 4 chunks of 16 B per thread (key = id/16, 8-dim chunk =
+  // id%16, id = tid + 256*i): whole 256-byte rows per 16 lanes.
+  // V: 4 consecutive keys x one 8-dim chunk per thread (chunk vc = tid/16, key
+  // quad kq = tid%16), so the transposed LDS write is one 8-byte store per dim.
   const bf16_t *kbase = a.k + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
   const bf16_t *vbase = a.v + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
   const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
-  const int kc0 = tid, kc1 = tid + kThreads;  // chunk ids: key = id/16, dchunk = id%16
-  const int vm = tid / 16, vc = tid % 16;     // V: keys 2vm, 2vm+1; dims 8vc..8vc+7
-  u32x4 kr0, kr1, vr0, vr1;
+  const int vc = tid / 16, kq = tid % 16;
+  u32x4 stg[4];
   uint8_t kvr = 0;
 
-  auto gload = [&](int key0) {
-    const int k0 = key0 + kc0 / 16, k1 = key0 + kc1 / 16;
-    kr0 = k0 < a.T ? *reinterpret_cast<const u32x4 *>(kbase + k0 * rstride + (kc0 % 16) * 8) : u32x4{0, 0, 0, 0};
-    kr1 = k1 < a.T ? *reinterpret_cast<const u32x4 *>(kbase + k1 * rstride + (kc1 % 16) * 8) : u32x4{0, 0, 0, 0};
-    const int v0 = key0 + 2 * vm, v1 = v0 + 1;
-    vr0 = v0 < a.T ? *reinterpret_cast<const u32x4 *>(vbase + v0 * rstride + vc * 8) : u32x4{0, 0, 0, 0};
-    vr1 = v1 < a.T ? *reinterpret_cast<const u32x4 *>(vbase + v1 * rstride + vc * 8) : u32x4{0, 0, 0, 0};
+  // K of the next tile is loaded at the start of an iteration and stored to LDS
+  // after the first 32-key half; V is loaded then and stored after the second
+  // half, so only one of the two stays in registers at a time.
+  auto load_k = [&](int key0) {
+    if (key0 + kBN <= a.T) {  // whole tile in range (block-uniform)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + kThreads * i;
+        stg[i] = *reinterpret_cast<const u32x4 *>(kbase + (key0 + c / 16) * rstride + (c % 16) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + kThreads * i;
+        const int kj = key0 + c / 16;
+        stg[i] = kj < a.T ? *reinterpret_cast<const u32x4 *>(kbase + kj * rstride + (c % 16) * 8) : u32x4{0, 0, 0, 0};
+      }
+    }
     if constexpr (kHasValid) {
       if (tid < kBN) kvr = (key0 + tid < a.T) ? a.key_valid[static_cast<int64_t>(b) * a.T + key0 + tid] : 0;
     }
   };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<u32x4 *>(&Ks[buf][kc0 / 16][(kc0 % 16) * 8]) = kr0;
-    *reinterpret_cast<u32x4 *>(&Ks[buf][kc1 / 16][(kc1 % 16) * 8]) = kr1;
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w0 = vr0[e], w1 = vr1[e];
-      // dims 8vc+2e (low halves) and 8vc+2e+1 (high halves) of keys 2vm, 2vm+1
-      *reinterpret_cast<uint32_t *>(&Vt[buf][8 * vc + 2 * e][2 * vm]) = (w0 & 0xffffu) | (w1 << 16);
-      *reinterpret_cast<uint32_t *>(&Vt[buf][8 * vc + 2 * e + 1][2 * vm]) = (w0 >> 16) | (w1 & 0xffff0000u);
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<u32x4 *>(&Ks[buf][k_lds_row(c / 16)][(c % 16) * 8]) = stg[i];
     }
     if constexpr (kHasValid) {
       if (tid < kBN) kvs[buf][tid] = kvr;
     }
   };
+  auto load_v = [&](int key0) {
+    if (key0 + kBN <= a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stg[i] = *reinterpret_cast<const u32x4 *>(vbase + (key0 + 4 * kq + i) * rstride + vc * 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int vj = key0 + 4 * kq + i;
+        stg[i] = vj < a.T ? *reinterpret_cast<const u32x4 *>(vbase + vj * rstride + vc * 8) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_v = [&](int buf) {
+    // V^T[d][4kq .. 4kq+3] for the 8 dims d = 8vc + e.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int wd = e >> 1;
+      uint32_t x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (e & 1) ? (stg[i][wd] >> 16) : (stg[i][wd] & 0xffffu);
+      const u32x2 w = {x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
+      *reinterpret_cast<u32x2 *>(&Vt[buf][8 * vc + e][4 * kq]) = w;
+    }
+  };
 
-  gload(0);
-  lstore(0);
+  load_k(0);
+  store_k(0);
+  load_v(0);
+  store_v(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int key0 = t * kBN;
-    if (t + 1 < ntiles) gload(key0 + kBN);
+    const bool more = t + 1 < ntiles;
+    if (more) load_k(key0 + kBN);
 
-    if (key0 <= wmax) {
-      // S^T for the 3 row blocks; K operand row for block kb:
-      //   key = 8*(lr/4) + 4*kb + (lr%4)  ->  acc slot v of lane l is key 8*lg + 4*kb + v.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && more) {
+        store_k(buf ^ 1);
+        load_v(key0 + kBN);
+      }
+      const int hk0 = key0 + 32 * h;  // first key of this half
+      if (hk0 > wmax) continue;       // wave-uniform: causally empty for this wave
+      // S^T for the 3 row blocks; accumulator slot v of lane l is key
+      // hk0 + 8*lg + 4*kb + v.
       f32x4 sacc[kRB][2];
 #pragma unroll
       for (int i = 0; i < kRB; ++i) sacc[i][0] = sacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int krow = 8 * (lr / 4) + 4 * kb + (lr % 4);
+        const bf16_t *krow = &Ks[buf][32 * h + 16 * kb + lr][8 * lg];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ks[buf][krow][32 * kk + 8 * lg]);
+          const bf16x8 af = *reinterpret_cast<const bf16x8 *>(krow + 32 * kk);
 #pragma unroll
           for (int i = 0; i < kRB; ++i)
             sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[i][kk], sacc[i][kb], 0, 0, 0);
         }
       }
       // softcap + shifted exp -> P (bf16) in the B-operand layout of P.V.
-      const bool diag = key0 + kBN - 1 > wmin;
+      const bool diag = hk0 + 31 > wmin;
       bf16x8 pf[kRB];
 #pragma unroll
       for (int i = 0; i < kRB; ++i) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float s = sacc[i][e >> 2][e & 3];
-          const float ex = __builtin_amdgcn_exp2f(s * a.k1);
+          const float sv = sacc[i][e >> 2][e & 3];
+          const float ex = __builtin_amdgcn_exp2f(sv * a.k1);
           const float r = __builtin_amdgcn_rcpf(1.f + ex);
           p[e] = __builtin_amdgcn_exp2f(a.k2 * r);
         }
         if (diag || kHasValid) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int key = key0 + 8 * lg + e;
+            const int key = hk0 + 8 * lg + e;
             bool ok = key <= pos[i];
-            if constexpr (kHasValid) ok = ok && kvs[buf][8 * lg + e] != 0;
+            if constexpr (kHasValid) ok = ok && kvs[buf][32 * h + 8 * lg + e] != 0;
             p[e] = ok ? p[e] : 0.f;
           }
         }
-        u32x4 w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
-                   cvt_pk_bf16(p[6], p[7])};
-        // The row sum adds the bf16-rounded weights that the P.V product uses,
-        // so the normalised weights of a row sum to one.
+        const u32x4 w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                         cvt_pk_bf16(p[6], p[7])};
+        pf[i] = __builtin_bit_cast(bf16x8, w);
+        // Row sum of the bf16-rounded weights that the P.V product uses, so the
+        // normalised weights of a row sum to one.
         float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ls += lo_bf16(w[e]) + hi_bf16(w[e]);
         lsum[i] += ls;
-        pf[i] = __builtin_bit_cast(bf16x8, w);
       }
       // O^T += V^T . P^T
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[buf][16 * db + lr][8 * lg]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[buf][16 * db + lr][32 * h + 8 * lg]);
 #pragma unroll
         for (int i = 0; i < kRB; ++i)
           oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], oacc[i][db], 0, 0, 0);
       }
     }
 
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    if (more) store_v(buf ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: row sums across the 4 lane groups, normalise, store bf16.
+  // Epilogue: normalise by the row sum and store bf16.
+  const bf16_t *vcol = vbase;
 #pragma unroll
   for (int i = 0; i < kRB; ++i) {
     float l = lsum[i];
@@ -244,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       for (int j = 0; j < a.T; ++j) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const u32x2 w = *reinterpret_cast<const u32x2 *>(vbase + j * rstride + 16 * db + 4 * lg);
+          const u32x2 w = *reinterpret_cast<const u32x2 *>(vcol + j * rstride + 16 * db + 4 * lg);
           acc[db][0] += lo_bf16(w[0]);
           acc[db][1] += hi_bf16(w[0]);
           acc[db][2] += lo_bf16(w[1]);

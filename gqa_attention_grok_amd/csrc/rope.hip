@@ -9,8 +9,8 @@
 // step[b] + t first, then K/V are written into the cache at that slot.
 //
 // Both kernels are HBM-bound elementwise passes. cos/sin depend only on
-// (position, pair), so a thread computes them once and reuses them for every
-// head of its token.
+// (position, pair), so they are computed once per token into LDS and shared by
+// every head of that token.
 #include <math.h>
 
 #include "common.h"
@@ -77,31 +77,32 @@ __device__ __forceinline__ void rope_head_chunk(const T *src, T *dst, int i0, in
   *reinterpret_cast<Vec<T, V> *>(dst + P + i0) = ob;
 }
 
-// grid.x = B*T tokens (grid-stride). Thread -> (pair chunk c, head lane hl).
+// grid.x = B*T tokens (grid-stride). Per token, the D/2 (cos, sin) pairs are
+// computed once into LDS, then the threads rotate (head, pair-chunk) items.
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void rope_kernel(T *x, int64_t ntok, int T_, int H, int D,
                                                         const int32_t *offset, RopeFreqs f) {
+  __shared__ float cs_s[256], sn_s[256];
   const int P = D / 2;
   const int nchunk = P / V;
-  const int hstride = kThreads / nchunk;
-  const int c = threadIdx.x % nchunk;
-  const int hl = threadIdx.x / nchunk;
-  if (hl >= hstride) return;
   for (int64_t tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
     const int b = static_cast<int>(tok / T_);
     const int t = static_cast<int>(tok % T_);
     const int pos = (offset ? offset[b] : 0) + t;
-    float cs[V], sn[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) phase_sincos(pos, f.inv[c * V + j], sn[j], cs[j]);
+    if (threadIdx.x < P) phase_sincos(pos, f.inv[threadIdx.x], sn_s[threadIdx.x], cs_s[threadIdx.x]);
+    __syncthreads();
     T *row = x + tok * static_cast<int64_t>(H) * D;
-    for (int h = hl; h < H; h += hstride)
+    for (int w = threadIdx.x; w < H * nchunk; w += kThreads) {
+      const int h = w / nchunk, c = w % nchunk;
       rope_head_chunk<T, V>(row + static_cast<int64_t>(h) * D, row + static_cast<int64_t>(h) * D,
-                            c * V, P, cs, sn);
+                            c * V, P, cs_s + c * V, sn_s + c * V);
+    }
+    __syncthreads();  // LDS reused by the next token
   }
 }
 
 // grid.x = B*T (one block per new token). Work items of a token:
+// (cos, sin) of the token's position are computed once into LDS.
 //   [0, Hq*nchunk)                     rotate q head chunks in place
 //   [.., + Hkv*nchunk)                 rotate k_new chunks into the cache
 //   [.., + Hkv*(D/8))                  copy v_new 16-byte chunks into the cache
@@ -121,6 +122,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
   if (!ok) return;
   const int pos = s0 + t;
   const int P = D / 2;
+  __shared__ float cs_s[256], sn_s[256];
+  if (do_rope && threadIdx.x < P) phase_sincos(pos, f.inv[threadIdx.x], sn_s[threadIdx.x], cs_s[threadIdx.x]);
+  __syncthreads();
   const int nchunk = P / V;
   const int nq = q ? Hq * nchunk : 0;
   const int nk = Hkv * nchunk;
@@ -140,10 +144,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
         dst = kc + (slot * Hkv + h) * D;
       }
       if (do_rope) {
-        float cs[V], sn[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) phase_sincos(pos, f.inv[c * V + j], sn[j], cs[j]);
-        rope_head_chunk<bf16_t, V>(src, dst, c * V, P, cs, sn);
+        rope_head_chunk<bf16_t, V>(src, dst, c * V, P, cs_s + c * V, sn_s + c * V);
       } else if (src != dst) {
         *reinterpret_cast<Vec<bf16_t, V> *>(dst + c * V) =
             *reinterpret_cast<const Vec<bf16_t, V> *>(src + c * V);

@@ -21,6 +21,19 @@ from . import (grok_attn_decode, grok_attn_decode_workspace_bytes, grok_attn_pre
                grok_kv_append, grok_linear_int8, grok_rmsnorm, grok_rope)
 
 
+def capture(step) -> "torch.cuda.CUDAGraph":
+    """Record one call of ``step`` into a HIP graph (torch's CUDAGraph API on
+    ROCm) so that it can be replayed without host launch overhead. The step's
+    kernels are launched on torch's current stream, which is the capture stream
+    inside the context; none of them records a memset."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
+
+
 class DecodeStep:
     def __init__(self, k_cache, v_cache, q, k_new, v_new, step, attn_mult, softcap=30.0,
                  rope_base=10000.0):
@@ -34,7 +47,7 @@ class DecodeStep:
         self.kv_len = torch.empty(B, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         nbytes = grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D)
-        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
     def __call__(self):
         grok_kv_append(self.k_cache, self.v_cache, self.k_new, self.v_new, self.step,

@@ -161,7 +161,8 @@ GROK_API int grok_attn_prefill(const void *q, const void *k, const void *v, int6
  *   q [B, 1, Hq, D]; caches [B, Tmax, Hkv, D]; kv_len [B] int32 device
  *   (= step + 1 after the new token was appended); out [B, 1, Hq*D]; bf16.
  *   workspace: device scratch of at least grok_attn_decode_workspace_bytes()
- *   bytes (split partial sums); its contents need no initialisation.
+ *   bytes (per-split partial sums); its contents need no initialisation. Calls
+ *   that overlap in time must not share a workspace.
  * A sequence with kv_len[b] outside [1, Tmax] gets an all-zero output row and
  * GROK_ERANGE is stored to *status.
  * Errors: EINVAL for NULL pointers, sizes < 1, Hq % Hkv != 0, Hq/Hkv > 16,
