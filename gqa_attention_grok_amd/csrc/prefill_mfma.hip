@@ -12,16 +12,23 @@
 //   Each wave owns 3 row blocks and walks the causal key range in tiles of 64
 //   keys, double-buffered in LDS (one barrier per tile).
 //
+// Data movement
+//   K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes per
+//   lane, no staging registers): while a tile is computed the next one is in
+//   flight. Rows are 256 bytes with the 16-byte chunks XOR-swizzled by row, so
+//   the fragment reads below are free of bank conflicts.
+//
 // MFMA formulation (v_mfma_f32_16x16x32_bf16), transposed so that each lane
 // always holds data of query row (lane % 16):
 //   S^T[key, row]  = K[key, :] . Q[row, :]^T          A = K (LDS), B = Q (regs)
 //   O^T[d, row]   += V^T[d, key] . P^T[key, row]      A = V^T (LDS), B = P (regs)
-//   The K rows feeding S^T are permuted so that the S^T accumulator of lane l
-//   holds keys 8*(l/16) .. 8*(l/16)+7 of a 32-key half for its row -- exactly
-//   the B-operand layout P needs for the P.V product, so P never leaves
-//   registers. The permutation is applied when K is stored into LDS, so the
-//   fragment reads walk consecutive rows. V is transposed while it is stored
-//   (4 keys per 8-byte LDS write).
+//   K rows are stored in the order the S^T A operand reads them (a permutation
+//   of each 32-key half) so that the S^T accumulator of lane l holds keys
+//   8*(l/16) .. 8*(l/16)+7 of the half for its row -- exactly the B-operand
+//   layout P needs for the P.V product, so P never leaves registers. The V^T
+//   A operand is read from row-major V with the LDS transpose read
+//   (ds_read_b64_tr_b16): in each group of 16 lanes, output lane 4a+j receives
+//   element j of the 4 elements addressed by source lanes a, a+4, a+8, a+12.
 //
 // Softmax without a running max: after the softcap every unmasked logit lies in
 // [-cap, cap], so p = exp(c - cap) is in [exp(-2cap), 1] -- no overflow, and no
@@ -43,12 +50,15 @@ constexpr int kWaves = 4;
 constexpr int kRB = 3;             // row blocks per wave
 constexpr int kRowBlocks = kWaves * kRB;
 constexpr int kBN = 64;            // keys per tile (two halves of 32 per MFMA step)
-constexpr int kKRow = kD + 8;      // padded LDS row of K: 272 B, 17 16-byte slots
-constexpr int kVRow = kBN + 8;     // padded LDS row of V^T: 144 B, 9 16-byte slots
+constexpr int kRowBytes = kD * 2;  // one K or V row in LDS (unpadded)
+constexpr int kTileBytes = kBN * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   f32x2 f = {a, b};
@@ -56,14 +66,20 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// LDS row of key j (0..63) in a K tile. The S^T MFMA of half h, key block kb
-// reads, in lane order, the keys 32h + 8*(r/4) + 4*kb + r%4 (r = lane % 16);
-// storing them at consecutive rows 32h + 16*kb + r makes those 16-byte reads
-// hit distinct bank groups.
-__device__ __forceinline__ int k_lds_row(int j) {
-  const int h = j >> 5, r = j & 31;
-  return 32 * h + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+// K tile layout: LDS row R holds key perm(R) (within each 32-key half, the
+// S^T A operand of key block kb reads keys 8*(r/4) + 4*kb + r%4 in lane order
+// r = lane%16; they sit at rows 16*kb + r). Chunk c (16 bytes) of row R is
+// stored at chunk c ^ (R % 8).
+__device__ __forceinline__ int k_row_key(int R) {  // key held by LDS row R
+  const int h = R >> 5, r = R & 31;
+  const int kb = r >> 4, a = (r >> 2) & 3, cc = r & 3;
+  return 32 * h + 8 * a + 4 * kb + cc;
 }
+__device__ __forceinline__ int k_byte(int R, int c) { return R * kRowBytes + ((c ^ (R & 7)) << 4); }
+// V tile layout: row r holds key r; chunk c is stored at chunk c ^ (2 * (r % 4)),
+// which keeps the two chunks of each 32-byte transpose-read span adjacent and
+// spreads the 16 rows of one transpose read over all banks.
+__device__ __forceinline__ int v_byte(int r, int c) { return r * kRowBytes + ((c ^ ((r & 3) << 1)) << 4); }
 
 struct PrefillArgs {
   const bf16_t *q, *k, *v;
@@ -76,8 +92,8 @@ struct PrefillArgs {
 
 template <bool kHasValid>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kBN][kKRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][kD][kVRow];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][kTileBytes];
   __shared__ uint8_t kvs[2][kBN];
 
   const int tid = threadIdx.x;
@@ -114,6 +130,45 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   }
   wmax = min(wmax, a.T - 1);
 
+  // Tile loads, HBM -> LDS. Each wave moves 4 KB of K and 4 KB of V per tile:
+  // instruction j (0..3) fills 1 KB = LDS rows 16*wave + 4*j .. +3, lane L
+  // writing physical chunk L%16 of row 16*wave + 4*j + L/16. Keys at or past T
+  // (ragged last tile) read row T-1 instead: they are masked out below.
+  const bf16_t *kbase = a.k + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
+  const bf16_t *vbase = a.v + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
+  const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
+  const int lrow = lane / 16, lchunk = lane % 16;
+  auto issue_tile = [&](int key0, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int R = 16 * wave + 4 * j + lrow;
+      const int kj = min(key0 + k_row_key(R), a.T - 1);
+      const int kc = lchunk ^ (R & 7);
+      __builtin_amdgcn_global_load_lds(kbase + kj * rstride + 8 * kc,
+                                       (lds_void *)(&Ks[buf][(16 * wave + 4 * j) * kRowBytes]),
+                                       16, 0, 0);
+      const int vj = min(key0 + R, a.T - 1);
+      const int vc = lchunk ^ ((R & 3) << 1);
+      __builtin_amdgcn_global_load_lds(vbase + vj * rstride + 8 * vc,
+                                       (lds_void *)(&Vs[buf][(16 * wave + 4 * j) * kRowBytes]),
+                                       16, 0, 0);
+    }
+  };
+  uint8_t kvr = 0;
+  auto load_valid = [&](int key0) {
+    if constexpr (kHasValid) {
+      if (tid < kBN) kvr = (key0 + tid < a.T) ? a.key_valid[static_cast<int64_t>(b) * a.T + key0 + tid] : 0;
+    }
+  };
+  auto store_valid = [&](int buf) {
+    if constexpr (kHasValid) {
+      if (tid < kBN) kvs[buf][tid] = kvr;
+    }
+  };
+
+  issue_tile(0, 0);
+  load_valid(0);
+
   // Q fragments (B operand of S^T): row lr, dims 32*kk + 8*lg .. +8.
   bf16x8 qf[kRB][4];
 #pragma unroll
@@ -136,93 +191,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     for (int db = 0; db < 8; ++db) oacc[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Tile staging. K: 4 chunks of 16 B per thread (key = id/16, 8-dim chunk =
-  // id%16, id = tid + 256*i): whole 256-byte rows per 16 lanes.
-  // V: 4 consecutive keys x one 8-dim chunk per thread (chunk vc = tid/16, key
-  // quad kq = tid%16), so the transposed LDS write is one 8-byte store per dim.
-  const bf16_t *kbase = a.k + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
-  const bf16_t *vbase = a.v + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
-  const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
-  const int vc = tid / 16, kq = tid % 16;
-  u32x4 stg[4];
-  uint8_t kvr = 0;
+  store_valid(0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS-bound loads have landed
+  __syncthreads();                // ... and everyone else's
 
-  // K of the next tile is loaded at the start of an iteration and stored to LDS
-  // after the first 32-key half; V is loaded then and stored after the second
-  // half, so only one of the two stays in registers at a time.
-  auto load_k = [&](int key0) {
-    if (key0 + kBN <= a.T) {  // whole tile in range (block-uniform)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + kThreads * i;
-        stg[i] = *reinterpret_cast<const u32x4 *>(kbase + (key0 + c / 16) * rstride + (c % 16) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + kThreads * i;
-        const int kj = key0 + c / 16;
-        stg[i] = kj < a.T ? *reinterpret_cast<const u32x4 *>(kbase + kj * rstride + (c % 16) * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-    if constexpr (kHasValid) {
-      if (tid < kBN) kvr = (key0 + tid < a.T) ? a.key_valid[static_cast<int64_t>(b) * a.T + key0 + tid] : 0;
-    }
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4 *>(&Ks[buf][k_lds_row(c / 16)][(c % 16) * 8]) = stg[i];
-    }
-    if constexpr (kHasValid) {
-      if (tid < kBN) kvs[buf][tid] = kvr;
-    }
-  };
-  auto load_v = [&](int key0) {
-    if (key0 + kBN <= a.T) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        stg[i] = *reinterpret_cast<const u32x4 *>(vbase + (key0 + 4 * kq + i) * rstride + vc * 8);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int vj = key0 + 4 * kq + i;
-        stg[i] = vj < a.T ? *reinterpret_cast<const u32x4 *>(vbase + vj * rstride + vc * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_v = [&](int buf) {
-    // V^T[d][4kq .. 4kq+3] for the 8 dims d = 8vc + e.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wd = e >> 1;
-      uint32_t x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (e & 1) ? (stg[i][wd] >> 16) : (stg[i][wd] & 0xffffu);
-      const u32x2 w = {x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
-      *reinterpret_cast<u32x2 *>(&Vt[buf][8 * vc + e][4 * kq]) = w;
-    }
-  };
-
-  load_k(0);
-  store_k(0);
-  load_v(0);
-  store_v(0);
-  __syncthreads();
+  // Per-lane pieces of the V^T transpose-read address: source lane s = lr of
+  // group lg points at key 8*lg + 4*hi + s/4 of the half, dims 16*db + 4*(s%4).
+  const int vrow0 = 8 * lg + lr / 4;
+  const int vsub = 8 * (lr & 1);     // byte offset inside the 16-byte chunk
+  const int vchunk = (lr & 3) >> 1;  // chunk within the 32-byte span of db
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int key0 = t * kBN;
     const bool more = t + 1 < ntiles;
-    if (more) load_k(key0 + kBN);
+    if (more) {
+      issue_tile(key0 + kBN, buf ^ 1);
+      load_valid(key0 + kBN);
+    }
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (h == 1 && more) {
-        store_k(buf ^ 1);
-        load_v(key0 + kBN);
-      }
       const int hk0 = key0 + 32 * h;  // first key of this half
       if (hk0 > wmax) continue;       // wave-uniform: causally empty for this wave
       // S^T for the 3 row blocks; accumulator slot v of lane l is key
@@ -232,10 +221,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       for (int i = 0; i < kRB; ++i) sacc[i][0] = sacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16_t *krow = &Ks[buf][32 * h + 16 * kb + lr][8 * lg];
+        const int R = 32 * h + 16 * kb + lr;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8 *>(krow + 32 * kk);
+          const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ks[buf][k_byte(R, 4 * kk + lg)]);
 #pragma unroll
           for (int i = 0; i < kRB; ++i)
             sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[i][kk], sacc[i][kb], 0, 0, 0);
@@ -273,22 +262,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
         for (int e = 0; e < 4; ++e) ls += lo_bf16(w[e]) + hi_bf16(w[e]);
         lsum[i] += ls;
       }
-      // O^T += V^T . P^T
+      // O^T += V^T . P^T; the V^T fragment of lane l (dim 16*db + lr, keys
+      // 8*lg .. 8*lg+7 of the half) comes from two transpose reads of 4 keys.
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[buf][16 * db + lr][32 * h + 8 * lg]);
+        const int r0 = 32 * h + vrow0, r1 = r0 + 4;
+        const int c = 2 * db + vchunk;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(&Vs[buf][v_byte(r0, c) + vsub]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(&Vs[buf][v_byte(r1, c) + vsub]));
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int i = 0; i < kRB; ++i)
           oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], oacc[i][db], 0, 0, 0);
       }
     }
 
-    if (more) store_v(buf ^ 1);
+    if (more) store_valid(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // next tile's LDS-bound loads have landed
     __syncthreads();
   }
 
   // Epilogue: normalise by the row sum and store bf16.
-  const bf16_t *vcol = vbase;
 #pragma unroll
   for (int i = 0; i < kRB; ++i) {
     float l = lsum[i];
@@ -304,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       for (int j = 0; j < a.T; ++j) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const u32x2 w = *reinterpret_cast<const u32x2 *>(vcol + j * rstride + 16 * db + 4 * lg);
+          const u32x2 w = *reinterpret_cast<const u32x2 *>(vbase + j * rstride + 16 * db + 4 * lg);
           acc[db][0] += lo_bf16(w[0]);
           acc[db][1] += hi_bf16(w[0]);
           acc[db][2] += lo_bf16(w[1]);
@@ -332,8 +328,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
 }
 
 int pick_gc(int G) {
-  for (int c = 12; c >= 1; --c)
-    if (G % c == 0 && 12 % c == 0) return c;
+  for (int c = kRowBlocks; c >= 1; --c)
+    if (G % c == 0 && kRowBlocks % c == 0) return c;
   return 1;
 }
 
@@ -367,11 +363,11 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int6
   const int64_t nblk = static_cast<int64_t>(B) * Hkv * a.nhc * a.nqt;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (key_valid)
-    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
-                       0, s, a);
+    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
-                     0, s, a);
+    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+                       s, a);
   return hipGetLastError();
 }
 
