@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="", help="comma list of c2,c3,c4,c5 (default: all)")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--only", default="", help="comma list of prefill,decode_b1,decode_ragged,sublayer (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (HBM counter calibration)")
@@ -96,7 +96,7 @@ def time_kernel(torch, fn, reps):
 
 
 def bench_prefill(torch, grok, pipe, U, gi, steps, warmup):
-    w = gi.WORKLOADS["c3_prefill_t8192"]
+    w = gi.WORKLOADS["prefill_b1_t8192"]
     p = gi.make_workload(w.name)
     st = pipe.PrefillStep(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), w.attn_mult,
                           w.softcap)
@@ -147,7 +147,7 @@ def bench_decode(torch, grok, pipe, U, gi, name, steps, warmup, replicas):
 
 
 def bench_sublayer(torch, grok, pipe, U, gi, steps, warmup):
-    w = gi.WORKLOADS["c5_sublayer_b4_t2048"]
+    w = gi.WORKLOADS["sublayer_b4_t2048"]
     p = gi.make_workload(w.name)
     dv = {k: (U.dev_bf16(v) if k == "x" else U.dev(v)) for k, v in p.items()}
     del p
@@ -164,12 +164,18 @@ def bench_sublayer(torch, grok, pipe, U, gi, steps, warmup):
 
 def cpu_baseline(gi, orc):
     """The fp64 oracle on a bounded sample of the 8k prefill: all 48 heads of
-    `n` query rows spread over the sequence (RoPE of the sampled q rows and of
+    256 query rows spread over the sequence (RoPE of the sampled q rows and of
     all keys, then the causal softcapped attention of those rows)."""
-    w = gi.WORKLOADS["c3_prefill_t8192"]
+    w = gi.WORKLOADS["prefill_b1_t8192"]
     p = gi.make_workload(w.name)
     T = w.T
-    rows = np.linspace(0, T - 1, 48).astype(np.int64)
+    rows = np.linspace(0, T - 1, 256).astype(np.int64)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):  # the oracle runs on one host core
+        return _cpu_baseline_sample(gi, orc, w, p, T, rows)
+
+
+def _cpu_baseline_sample(gi, orc, w, p, T, rows):
     t0 = time.perf_counter()
     k = orc.rope(orc.bf16_bits_to_f64(p["k"]), np.arange(T)[None], out="bf16")
     v = orc.bf16_bits_to_f64(p["v"])
@@ -201,7 +207,7 @@ def main():
     import gqa_inputs as gi
     import gpu_util as U
 
-    only = set(args.only.split(",")) if args.only else {"c2", "c3", "c4", "c5"}
+    only = set(args.only.split(",")) if args.only else {"prefill", "decode_b1", "decode_ragged", "sublayer"}
     res = {}
     if args.copy_calibration:
         # a plain copy of known size: reads and writes exactly 256 MiB
@@ -212,24 +218,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         print("# copy calibration done: 268435456 bytes read and written", file=sys.stderr, flush=True)
-    if "c3" in only:
-        res["c3"] = bench_prefill(torch, grok, pipe, U, gi, args.steps, args.warmup)
-        print(f"# c3 done: {res['c3']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if "prefill" in only:
+        res["prefill"] = bench_prefill(torch, grok, pipe, U, gi, args.steps, args.warmup)
+        print(f"# prefill done: {res['prefill']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-    if "c2" in only:
-        res["c2"] = bench_decode(torch, grok, pipe, U, gi, "c2_decode_b1", args.steps, args.warmup, 16)
-        print(f"# c2 done: {res['c2']['value']:.1f} GB/s", file=sys.stderr, flush=True)
+    if "decode_b1" in only:
+        res["decode_b1"] = bench_decode(torch, grok, pipe, U, gi, "decode_b1_t8192", args.steps, args.warmup, 16)
+        print(f"# decode_b1 done: {res['decode_b1']['value']:.1f} GB/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-    if "c4" in only:
-        res["c4"] = bench_decode(torch, grok, pipe, U, gi, "c4_decode_ragged_b32", args.steps,
+    if "decode_ragged" in only:
+        res["decode_ragged"] = bench_decode(torch, grok, pipe, U, gi, "decode_ragged_b32_t8192", args.steps,
                                  args.warmup, 2)
-        print(f"# c4 done: {res['c4']['value']:.1f} GB/s", file=sys.stderr, flush=True)
+        print(f"# decode_ragged done: {res['decode_ragged']['value']:.1f} GB/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-    if "c5" in only:
-        res["c5"] = bench_sublayer(torch, grok, pipe, U, gi, max(1, args.steps // 4), min(args.warmup, 2))
-        print(f"# c5 done: {res['c5']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if "sublayer" in only:
+        res["sublayer"] = bench_sublayer(torch, grok, pipe, U, gi, max(1, args.steps // 4), min(args.warmup, 2))
+        print(f"# sublayer done: {res['sublayer']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    head = res.get("c3") or next(iter(res.values()))
+    head = res.get("prefill") or next(iter(res.values()))
     line = {
         "metric": METRIC,
         "value": round(head["value"], 3),
@@ -245,9 +251,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": head["workload"] + (
             ": causal GQA prefill B=1 T=8192 Hq=48 Hkv=8 D=128 bf16, step = RoPE(Q,K) + attention"
-            if head is res.get("c3") else "")},
+            if head is res.get("prefill") else "")},
     }
-    if head is res.get("c3"):
+    if head is res.get("prefill"):
         tr = traffic_for(head["kernel"])
         line["roofline"] = {
             "kernel": head["kernel"], "bound": "mfma", "achieved": round(head["kernel_tflops"], 3),

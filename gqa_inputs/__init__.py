@@ -103,24 +103,24 @@ class Workload:
 
 WORKLOADS = {
     # Tiny fp32 causal prefill: one KV head shared by six query heads.
-    "c1_tiny_prefill_f32": Workload(
-        name="c1_tiny_prefill_f32", kind="prefill", seed=1001, dtype="f32",
+    "prefill_f32_t16": Workload(
+        name="prefill_f32_t16", kind="prefill", seed=1001, dtype="f32",
         B=1, T=16, Hq=6, Hkv=1, D=32),
     # Single-token decode against a full 8192-slot cache.
-    "c2_decode_b1": Workload(
-        name="c2_decode_b1", kind="decode", seed=1002, dtype="bf16",
+    "decode_b1_t8192": Workload(
+        name="decode_b1_t8192", kind="decode", seed=1002, dtype="bf16",
         B=1, Hq=48, Hkv=8, D=128, Tmax=8192),
     # 8k causal prefill with the logit multiplier raised 4x.
-    "c3_prefill_t8192": Workload(
-        name="c3_prefill_t8192", kind="prefill", seed=1003, dtype="bf16",
+    "prefill_b1_t8192": Workload(
+        name="prefill_b1_t8192", kind="prefill", seed=1003, dtype="bf16",
         B=1, T=8192, Hq=48, Hkv=8, D=128, logit_scale_factor=4.0),
     # 32 sequences of lengths uniform in [512, 8192], one new token each.
-    "c4_decode_ragged_b32": Workload(
-        name="c4_decode_ragged_b32", kind="decode", seed=1004, dtype="bf16",
+    "decode_ragged_b32_t8192": Workload(
+        name="decode_ragged_b32_t8192", kind="decode", seed=1004, dtype="bf16",
         B=32, Hq=48, Hkv=8, D=128, Tmax=8192, ragged=True),
     # Full attention sub-layer: norm, int8 projections, RoPE, attention, norm.
-    "c5_sublayer_b4_t2048": Workload(
-        name="c5_sublayer_b4_t2048", kind="sublayer", seed=1005, dtype="bf16",
+    "sublayer_b4_t2048": Workload(
+        name="sublayer_b4_t2048", kind="sublayer", seed=1005, dtype="bf16",
         B=4, T=2048, Hq=48, Hkv=8, D=128, d_model=6144),
 }
 

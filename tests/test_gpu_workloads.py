@@ -23,9 +23,9 @@ def G():
     return grok, pipe, gpu_util, torch
 
 
-def test_c1_tiny_prefill_f32(G):
+def test_prefill_f32_t16(G):
     grok, pipe, U, torch = G
-    w = gi.WORKLOADS["c1_tiny_prefill_f32"]
+    w = gi.WORKLOADS["prefill_f32_t16"]
     p = gi.make_workload(w.name)
     step = pipe.PrefillStep(U.dev(p["q"]), U.dev(p["k"]), U.dev(p["v"]), w.attn_mult, w.softcap)
     out = U.host(step())
@@ -34,8 +34,8 @@ def test_c1_tiny_prefill_f32(G):
     k = orc.rope(p["k"].astype(np.float64), pos, out="f32")
     ref = orc.attention(q, k, p["v"].astype(np.float64), orc.attention_mask(pos, w.T), w.attn_mult,
                         w.softcap)
-    err = U.assert_f32_close(out, ref, "c1")
-    print(f"c1 max abs err {err:.2e}")
+    err = U.assert_f32_close(out, ref, "tiny prefill")
+    print(f"tiny prefill max abs err {err:.2e}")
 
 
 def _decode_check(G, name):
@@ -83,17 +83,17 @@ def _decode_check(G, name):
     print(f"{name} max abs err {max(errs):.2e}")
 
 
-def test_c2_decode_b1(G):
-    _decode_check(G, "c2_decode_b1")
+def test_decode_b1_t8192(G):
+    _decode_check(G, "decode_b1_t8192")
 
 
-def test_c4_decode_ragged_b32(G):
-    _decode_check(G, "c4_decode_ragged_b32")
+def test_decode_ragged_b32_t8192(G):
+    _decode_check(G, "decode_ragged_b32_t8192")
 
 
-def test_c3_prefill_t8192_sampled(G):
+def test_prefill_b1_t8192_sampled(G):
     grok, pipe, U, torch = G
-    w = gi.WORKLOADS["c3_prefill_t8192"]
+    w = gi.WORKLOADS["prefill_b1_t8192"]
     p = gi.make_workload(w.name)
     step = pipe.PrefillStep(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), w.attn_mult,
                             w.softcap)
@@ -115,13 +115,13 @@ def test_c3_prefill_t8192_sampled(G):
         mask_row = np.arange(T) <= t
         for h in range(Hq):
             ref = orc.attention_rows(qt, k, v, 0, 0, h, mask_row, w.attn_mult, w.softcap)
-            errs.append(U.assert_bf16_close(got[r, h], ref, f"c3 t={t} h={h}"))
-    print(f"c3 sampled {len(rows)} rows x {Hq} heads, max abs err {max(errs):.2e}")
+            errs.append(U.assert_bf16_close(got[r, h], ref, f"prefill t={t} h={h}"))
+    print(f"prefill sampled {len(rows)} rows x {Hq} heads, max abs err {max(errs):.2e}")
 
 
 def test_c5_sublayer_sampled(G):
     grok, pipe, U, torch = G
-    w = gi.WORKLOADS["c5_sublayer_b4_t2048"]
+    w = gi.WORKLOADS["sublayer_b4_t2048"]
     p = gi.make_workload(w.name)
     dv = {k: (U.dev_bf16(v) if k == "x" else U.dev(v)) for k, v in p.items()}
     step = pipe.SublayerStep(dv["x"], dv["wq"], dv["sq"], dv["wk"], dv["sk"], dv["wv"], dv["sv"],
@@ -131,15 +131,15 @@ def test_c5_sublayer_sampled(G):
     B, T, d, Hq, Hkv, D = w.B, w.T, w.d_model, w.Hq, w.Hkv, w.D
     x = orc.bf16_bits_to_f64(p["x"])
     n = orc.rmsnorm(x, None, w.eps, out="bf16")
-    U.assert_bf16_close(U.host(step.n), orc.rmsnorm(x, None, w.eps), "c5 pre-norm")
+    U.assert_bf16_close(U.host(step.n), orc.rmsnorm(x, None, w.eps), "sublayer pre-norm")
     g = gi.rng(4242)
     errs = []
     for b in (0, 3):
         kb = orc.linear_int8(n[b], p["wk"], p["sk"], out="bf16").reshape(1, T, Hkv, D)
         vb = orc.linear_int8(n[b], p["wv"], p["sv"]).reshape(1, T, Hkv, D)
-        U.assert_bf16_close(U.host(step.v[b:b + 1]), vb, "c5 v projection")
+        U.assert_bf16_close(U.host(step.v[b:b + 1]), vb, "sublayer v projection")
         vb = orc.round_bf16(vb)
-        U.assert_bf16_close(U.host(step.k[b:b + 1]), orc.rope(kb, np.arange(T)[None]), "c5 roped k")
+        U.assert_bf16_close(U.host(step.k[b:b + 1]), orc.rope(kb, np.arange(T)[None]), "sublayer roped k")
         kb = orc.rope(kb, np.arange(T)[None], out="bf16")
         for t in [0, 1, 2047] + list(g.integers(0, T, 5)):
             qt = orc.linear_int8(n[b, t], p["wq"], p["sq"], out="bf16").reshape(1, 1, Hq, D)
@@ -148,13 +148,13 @@ def test_c5_sublayer_sampled(G):
             a = np.concatenate([orc.attention_rows(qt, kb, vb, 0, 0, h, mask_row, w.attn_mult, w.softcap)
                                 for h in range(Hq)])
             ga = U.host(step.attn[b, t])
-            U.assert_bf16_close(ga, a, f"c5 attention b={b} t={t}")
+            U.assert_bf16_close(ga, a, f"sublayer attention b={b} t={t}")
             a = orc.round_bf16(a)
             o = orc.linear_int8(a, p["wo"], p["so"])
             go = U.host(step.o[b, t])
-            print(f"c5 b={b} t={t}: rel L2 attention {U.rel_l2(ga, a):.2e}, "
+            print(f"sublayer b={b} t={t}: rel L2 attention {U.rel_l2(ga, a):.2e}, "
                   f"out-proj {U.rel_l2(go, o):.2e}", flush=True)
-            U.assert_bf16_close(go, o, f"c5 output projection b={b} t={t}")
+            U.assert_bf16_close(go, o, f"sublayer output projection b={b} t={t}")
             o = orc.round_bf16(o)
             # post-norm handed on in bf16, then the residual add (exact; the GPU rounds it)
             nt = orc.rmsnorm(o[None], None, w.eps, out="bf16")[0]
@@ -163,6 +163,6 @@ def test_c5_sublayer_sampled(G):
             # part of the bound applies to the larger of |y| and the normalised
             # summand |n|: when x and n nearly cancel, |y| is small while n
             # carries its own bf16 error at its own magnitude.
-            errs.append(U.assert_bf16_close(U.host(y[b, t]), yt, f"c5 output b={b} t={t}",
+            errs.append(U.assert_bf16_close(U.host(y[b, t]), yt, f"sublayer output b={b} t={t}",
                                             magnitude=np.maximum(np.abs(yt), np.abs(nt))))
-    print(f"c5 sampled rows, max abs err {max(errs):.2e}")
+    print(f"sublayer sampled rows, max abs err {max(errs):.2e}")
