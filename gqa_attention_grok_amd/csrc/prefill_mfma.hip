@@ -39,6 +39,8 @@
 // Masked logits give p = 0 exactly. A row with no unmasked key (only possible
 // with key padding) takes the -1e30 semantics of the pages: the uniform mean
 // of all T value rows, computed in the epilogue for such rows only.
+#include <utility>
+
 #include "common.h"
 
 namespace grok {
@@ -56,9 +58,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// acc + lo + hi of a packed bf16 pair in one instruction (v_dot2c_f32_bf16
+// against the pair (1.0, 1.0)). Inline assembly: this compiler's
+// __builtin_amdgcn_fdot2_f32_bf16 passes the same 32-bit source for every
+// element of a vector it is given.
+__device__ __forceinline__ float add_bf16_pair(float acc, uint32_t pair) {
+  asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(pair));
+  return acc;
+}
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   f32x2 f = {a, b};
@@ -78,8 +88,45 @@ __device__ __forceinline__ int k_row_key(int R) {  // key held by LDS row R
 __device__ __forceinline__ int k_byte(int R, int c) { return R * kRowBytes + ((c ^ (R & 7)) << 4); }
 // V tile layout: row r holds key r; chunk c is stored at chunk c ^ (2 * (r % 4)),
 // which keeps the two chunks of each 32-byte transpose-read span adjacent and
-// spreads the 16 rows of one transpose read over all banks.
+// spreads the 16 rows of one transpose read over all banks. For the P.V operand
+// (c = 2*db + (0|1), rows r and r + 4 with the same r % 4 = s) this places
+// dims block db = 4*k + m at byte 128*k + 32*(m ^ s) + 16*(c & 1) of the row.
 __device__ __forceinline__ int v_byte(int r, int c) { return r * kRowBytes + ((c ^ ((r & 3) << 1)) << 4); }
+
+// LDS transpose read (ds_read_b64_tr_b16) at addr + kOff. Written as inline
+// assembly because the compiler treats the builtin form as possibly aliasing
+// the in-flight global_load_lds of the next tile and waits for those loads
+// before the first read, which would serialise the prefetch with the P.V
+// product. The asm is invisible to the compiler's LDS counter tracking, so its
+// results are only used after an explicit wait (lds_wait) that takes them as
+// operands. LDS operations complete in issue order, so the compiler's own
+// waits stay correct with these reads in flight.
+template <int kOff>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff) : "memory");
+  return r;
+}
+
+// The 16 reads of one 32-key half: lo/hi[db] for dims 16*db .. 16*db + 15,
+// keys 8*(lane/16) + 0..3 (lo) and + 4..7 (hi, 4 rows = 1024 bytes further).
+template <int kHalfOff, int... kDb>
+__device__ __forceinline__ void read_vt_half(u32x2 *lo, u32x2 *hi, const uint32_t *am,
+                                             std::integer_sequence<int, kDb...>) {
+  ((lo[kDb] = lds_read_tr16<kHalfOff + 128 * (kDb / 4)>(am[kDb % 4]),
+    hi[kDb] = lds_read_tr16<kHalfOff + 128 * (kDb / 4) + 1024>(am[kDb % 4])),
+   ...);
+}
+
+// Waits until at most kLeft LDS operations are outstanding; the four fragment
+// pairs pass through so that no use of them is scheduled above the wait.
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(u32x2 *lo, u32x2 *hi) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]), "+v"(hi[0]), "+v"(hi[1]),
+                 "+v"(hi[2]), "+v"(hi[3])
+               : "i"(kLeft));
+}
 
 struct PrefillArgs {
   const bf16_t *q, *k, *v;
@@ -87,7 +134,7 @@ struct PrefillArgs {
   bf16_t *out;
   int64_t kv_rows;
   int B, T, Hq, Hkv, G, Gc, npb, nhc, nqt;
-  float k1, k2;  // exp2 scale inside the softcap, outer exp2 scale
+  float k1, k2inv;  // exp2 scale inside the softcap; 1 / (outer exp2 scale)
 };
 
 template <bool kHasValid>
@@ -98,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform, in an SGPR
   const int lr = lane % 16;  // this lane's row inside a row block
   const int lg = lane / 16;  // this lane's k/key group
 
@@ -132,13 +179,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
 
   // Tile loads, HBM -> LDS. Each wave moves 4 KB of K and 4 KB of V per tile:
   // instruction j (0..3) fills 1 KB = LDS rows 16*wave + 4*j .. +3, lane L
-  // writing physical chunk L%16 of row 16*wave + 4*j + L/16. Keys at or past T
-  // (ragged last tile) read row T-1 instead: they are masked out below.
+  // writing physical chunk L%16 of row 16*wave + 4*j + L/16. Row R of the K tile
+  // holds key k_row_key(R), which for these rows is key_l + 8*j; its chunk
+  // swizzle (R % 8 = 4*(j%2) + L/16) alternates with the parity of j. Row R of
+  // the V tile holds key R, with swizzle 2*(L/16) for every j. So one per-lane
+  // byte offset per K parity and one for V, plus a wave-uniform base, address
+  // all eight loads. Keys at or past T (ragged last tile) read row T-1 instead:
+  // they are masked out below.
   const bf16_t *kbase = a.k + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
   const bf16_t *vbase = a.v + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
   const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
+  const uint32_t rs2 = static_cast<uint32_t>(rstride) * 2;  // bytes between key rows
   const int lrow = lane / 16, lchunk = lane % 16;
+  const int key_l = 32 * (wave >> 1) + 4 * (wave & 1) + lrow;
+  const uint32_t koff_e = key_l * rs2 + 16 * (lchunk ^ lrow);
+  const uint32_t koff_o = key_l * rs2 + 16 * (lchunk ^ (4 + lrow));
+  const uint32_t voff = (16 * wave + lrow) * rs2 + 16 * (lchunk ^ (lrow << 1));
   auto issue_tile = [&](int key0, int buf) {
+    if (key0 + kBN <= a.T) {
+      const char *kt = reinterpret_cast<const char *>(kbase) + static_cast<int64_t>(key0) * rs2;
+      const char *vt = reinterpret_cast<const char *>(vbase) + static_cast<int64_t>(key0 + 16 * wave) * rs2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_global_load_lds(kt + 8 * j * rs2 + ((j & 1) ? koff_o : koff_e),
+                                         (lds_void *)(&Ks[buf][(16 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + 4 * j * rs2 + (voff - 16 * wave * rs2),
+                                         (lds_void *)(&Vs[buf][(16 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int R = 16 * wave + 4 * j + lrow;
@@ -195,25 +264,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS-bound loads have landed
   __syncthreads();                // ... and everyone else's
 
-  // Per-lane pieces of the V^T transpose-read address: source lane s = lr of
-  // group lg points at key 8*lg + 4*hi + s/4 of the half, dims 16*db + 4*(s%4).
-  const int vrow0 = 8 * lg + lr / 4;
-  const int vsub = 8 * (lr & 1);     // byte offset inside the 16-byte chunk
-  const int vchunk = (lr & 3) >> 1;  // chunk within the 32-byte span of db
+  // Per-lane V^T transpose-read addresses: source lane s = lr of group lg points
+  // at key 8*lg + s/4 of the half (+4 for hi), dims 16*db + 4*(s%4); am[m]
+  // covers dims blocks db = m and m + 4 of Vs[0] (v_byte with the swizzle
+  // term folded in).
+  uint32_t am[4];
+  {
+    const int vrow0 = 8 * lg + lr / 4;
+    const int vs = vrow0 & 3;
+    const uint32_t vbase0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Vs[0][0])));
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      am[m] = vbase0 + vrow0 * kRowBytes + 32 * (m ^ vs) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+  }
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile of 64 keys. kMask: apply the causal (and key-valid) mask; tiles
+  // wholly below the workgroup's first query row need none and run without it,
+  // as one branch-free block the scheduler can interleave freely.
+  auto tile = [&](int t, auto mask_c) {
+    constexpr bool kMask = decltype(mask_c)::value;
     const int buf = t & 1;
     const int key0 = t * kBN;
-    const bool more = t + 1 < ntiles;
+    const bool more = !kMask || t + 1 < ntiles;  // unmasked tiles always have a successor
     if (more) {
       issue_tile(key0 + kBN, buf ^ 1);
       load_valid(key0 + kBN);
     }
-
+    uint32_t amb[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int m = 0; m < 4; ++m) amb[m] = am[m] + buf * kTileBytes;
+
+    auto half = [&](auto hconst) {
+      constexpr int h = decltype(hconst)::value;
       const int hk0 = key0 + 32 * h;  // first key of this half
-      if (hk0 > wmax) continue;       // wave-uniform: causally empty for this wave
+      if (kMask && hk0 > wmax) return;  // wave-uniform: causally empty for this wave
       // S^T for the 3 row blocks; accumulator slot v of lane l is key
       // hk0 + 8*lg + 4*kb + v.
       f32x4 sacc[kRB][2];
@@ -230,8 +314,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
             sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[i][kk], sacc[i][kb], 0, 0, 0);
         }
       }
-      // softcap + shifted exp -> P (bf16) in the B-operand layout of P.V.
-      const bool diag = hk0 + 31 > wmin;
+      // softcap + shifted exp -> P (bf16) in the B-operand layout of P.V:
+      // p = exp2(k2 / (1 + exp2(k1*s))) = exp2(rcp((1 + e) * (1/k2))).
+      const bool diag = kMask && hk0 + 31 > wmin;
       bf16x8 pf[kRB];
 #pragma unroll
       for (int i = 0; i < kRB; ++i) {
@@ -240,10 +325,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
         for (int e = 0; e < 8; ++e) {
           const float sv = sacc[i][e >> 2][e & 3];
           const float ex = __builtin_amdgcn_exp2f(sv * a.k1);
-          const float r = __builtin_amdgcn_rcpf(1.f + ex);
-          p[e] = __builtin_amdgcn_exp2f(a.k2 * r);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(__builtin_fmaf(ex, a.k2inv, a.k2inv)));
         }
-        if (diag || kHasValid) {
+        if (diag || (kMask && kHasValid)) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int key = hk0 + 8 * lg + e;
@@ -255,34 +339,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
         const u32x4 w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                          cvt_pk_bf16(p[6], p[7])};
         pf[i] = __builtin_bit_cast(bf16x8, w);
-        // Row sum of the bf16-rounded weights that the P.V product uses, so the
-        // normalised weights of a row sum to one.
-        float ls = 0.f;
+        // Row sum of the bf16-rounded weights that the P.V product uses (so the
+        // normalised weights of a row sum to one): bf16 pair dot (1, 1).
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ls += lo_bf16(w[e]) + hi_bf16(w[e]);
-        lsum[i] += ls;
+        for (int e = 0; e < 4; ++e) lsum[i] = add_bf16_pair(lsum[i], w[e]);
       }
       // O^T += V^T . P^T; the V^T fragment of lane l (dim 16*db + lr, keys
       // 8*lg .. 8*lg+7 of the half) comes from two transpose reads of 4 keys.
+      u32x2 lo[8], hi[8];
+      read_vt_half<h * 32 * kRowBytes>(lo, hi, amb, std::make_integer_sequence<int, 8>{});
+      lds_wait<8>(lo, hi);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const int r0 = 32 * h + vrow0, r1 = r0 + 4;
-        const int c = 2 * db + vchunk;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4 *)(&Vs[buf][v_byte(r0, c) + vsub]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4 *)(&Vs[buf][v_byte(r1, c) + vsub]));
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        if (db == 4) lds_wait<0>(lo + 4, hi + 4);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[db][0], lo[db][1], hi[db][0], hi[db][1]});
 #pragma unroll
         for (int i = 0; i < kRB; ++i)
           oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], oacc[i][db], 0, 0, 0);
       }
-    }
+    };
+    half(std::integral_constant<int, 0>{});
+    half(std::integral_constant<int, 1>{});
 
     if (more) store_valid(buf ^ 1);
     __builtin_amdgcn_s_waitcnt(0);  // next tile's LDS-bound loads have landed
     __syncthreads();
-  }
+  };
+
+  // Tiles [0, tfull) end below the workgroup's first query row p0.
+  const int tfull = kHasValid ? 0 : p0 / kBN;
+  int t = 0;
+  for (; t < tfull; ++t) tile(t, std::false_type{});
+  for (; t < ntiles; ++t) tile(t, std::true_type{});
 
   // Epilogue: normalise by the row sum and store bf16.
 #pragma unroll
@@ -359,7 +447,7 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int6
   a.nhc = a.G / a.Gc;
   a.nqt = (T + 16 * a.npb - 1) / (16 * a.npb);
   a.k1 = 2.f * mult * kLog2e / cap;
-  a.k2 = -2.f * cap * kLog2e;
+  a.k2inv = 1.f / (-2.f * cap * kLog2e);
   const int64_t nblk = static_cast<int64_t>(B) * Hkv * a.nhc * a.nqt;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (key_valid)

@@ -119,7 +119,7 @@ def test_prefill_b1_t8192_sampled(G):
     print(f"prefill sampled {len(rows)} rows x {Hq} heads, max abs err {max(errs):.2e}")
 
 
-def test_c5_sublayer_sampled(G):
+def test_sublayer_b4_t2048_sampled(G):
     grok, pipe, U, torch = G
     w = gi.WORKLOADS["sublayer_b4_t2048"]
     p = gi.make_workload(w.name)
