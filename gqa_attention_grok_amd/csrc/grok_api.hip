@@ -123,7 +123,7 @@ int grok_attn_prefill(const void *q, const void *k, const void *v, int64_t kv_ro
   if (!q || !k || !v || !out) return fail(GROK_EINVAL, "attn_prefill: null pointer");
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
-  if (grok::prefill_mfma_supported(Hq, Hkv, D, dtype)) {
+  if (grok::prefill_mfma_supported(kv_rows, Hq, Hkv, D, dtype)) {
     if (al % 16) return fail(GROK_EINVAL, "attn_prefill: misaligned pointer");
     return hip_status(grok::launch_prefill_mfma(q, k, v, kv_rows, key_valid, out, B, T, Hq, Hkv,
                                                 attn_mult, softcap, stream),

@@ -76,22 +76,31 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// LDS bank layout. A 256-byte row spans all 64 four-byte banks of the LDS, so
+// which banks an access hits depends only on the 16-byte chunk position within
+// the row; chunks are XOR-swizzled by row so that the lanes served together by
+// one fragment read hit distinct banks (16 lanes for a 16-byte read, 32 for an
+// 8-byte read; the same holds for a 32-bank, 128-byte-per-cycle organisation).
+//
 // K tile layout: LDS row R holds key perm(R) (within each 32-key half, the
 // S^T A operand of key block kb reads keys 8*(r/4) + 4*kb + r%4 in lane order
 // r = lane%16; they sit at rows 16*kb + r). Chunk c (16 bytes) of row R is
-// stored at chunk c ^ (R % 8).
+// stored at chunk c ^ (R % 16): the 16 rows of one read land on 16 chunks.
 __device__ __forceinline__ int k_row_key(int R) {  // key held by LDS row R
   const int h = R >> 5, r = R & 31;
   const int kb = r >> 4, a = (r >> 2) & 3, cc = r & 3;
   return 32 * h + 8 * a + 4 * kb + cc;
 }
-__device__ __forceinline__ int k_byte(int R, int c) { return R * kRowBytes + ((c ^ (R & 7)) << 4); }
-// V tile layout: row r holds key r; chunk c is stored at chunk c ^ (2 * (r % 4)),
-// which keeps the two chunks of each 32-byte transpose-read span adjacent and
-// spreads the 16 rows of one transpose read over all banks. For the P.V operand
-// (c = 2*db + (0|1), rows r and r + 4 with the same r % 4 = s) this places
-// dims block db = 4*k + m at byte 128*k + 32*(m ^ s) + 16*(c & 1) of the row.
-__device__ __forceinline__ int v_byte(int r, int c) { return r * kRowBytes + ((c ^ ((r & 3) << 1)) << 4); }
+__device__ __forceinline__ int k_byte(int R, int c) { return R * kRowBytes + ((c ^ (R & 15)) << 4); }
+// V tile layout: row r holds key r; chunk c is stored at chunk c ^ (2 * g(r)),
+// g(r) = (r % 4) + 4 * ((r / 8) % 2). The even XOR keeps the two chunks of each
+// 32-byte transpose-read span adjacent; one 32-lane pass of a transpose read
+// covers rows {0..3, 8..11} (+4, +16, +32 ...), whose g are all distinct, so
+// its eight 32-byte spans fill the 64 banks. For the P.V operand
+// (c = 2*db + (0|1), rows r and r + 4 with the same g) dims block db sits at
+// byte 32*(db ^ g(r)) + 16*(c & 1) of the row.
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3); }
+__device__ __forceinline__ int v_byte(int r, int c) { return r * kRowBytes + ((c ^ v_swz(r)) << 4); }
 
 // LDS transpose read (ds_read_b64_tr_b16) at addr + kOff. Written as inline
 // assembly because the compiler treats the builtin form as possibly aliasing
@@ -109,12 +118,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
 }
 
 // The 16 reads of one 32-key half: lo/hi[db] for dims 16*db .. 16*db + 15,
-// keys 8*(lane/16) + 0..3 (lo) and + 4..7 (hi, 4 rows = 1024 bytes further).
+// keys 8*(lane/16) + 0..3 (lo) and + 4..7 (hi, 4 rows = 1024 bytes further);
+// am[db] is this lane's address of dims block db in the tile's first half.
 template <int kHalfOff, int... kDb>
 __device__ __forceinline__ void read_vt_half(u32x2 *lo, u32x2 *hi, const uint32_t *am,
                                              std::integer_sequence<int, kDb...>) {
-  ((lo[kDb] = lds_read_tr16<kHalfOff + 128 * (kDb / 4)>(am[kDb % 4]),
-    hi[kDb] = lds_read_tr16<kHalfOff + 128 * (kDb / 4) + 1024>(am[kDb % 4])),
+  ((lo[kDb] = lds_read_tr16<kHalfOff>(am[kDb]), hi[kDb] = lds_read_tr16<kHalfOff + 1024>(am[kDb])),
    ...);
 }
 
@@ -192,18 +201,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   const uint32_t rs2 = static_cast<uint32_t>(rstride) * 2;  // bytes between key rows
   const int lrow = lane / 16, lchunk = lane % 16;
   const int key_l = 32 * (wave >> 1) + 4 * (wave & 1) + lrow;
-  const uint32_t koff_e = key_l * rs2 + 16 * (lchunk ^ lrow);
-  const uint32_t koff_o = key_l * rs2 + 16 * (lchunk ^ (4 + lrow));
-  const uint32_t voff = (16 * wave + lrow) * rs2 + 16 * (lchunk ^ (lrow << 1));
+  const uint32_t koff = key_l * rs2;
+  const uint32_t voff = lrow * rs2;
   auto issue_tile = [&](int key0, int buf) {
     if (key0 + kBN <= a.T) {
       const char *kt = reinterpret_cast<const char *>(kbase) + static_cast<int64_t>(key0) * rs2;
       const char *vt = reinterpret_cast<const char *>(vbase) + static_cast<int64_t>(key0 + 16 * wave) * rs2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_global_load_lds(kt + 8 * j * rs2 + ((j & 1) ? koff_o : koff_e),
+        // R % 16 = 4*j + L/16; v_swz(R) = 2*(L/16) + 8*(j/2)
+        __builtin_amdgcn_global_load_lds(kt + 8 * j * rs2 + (koff + 16 * (lchunk ^ (4 * j + lrow))),
                                          (lds_void *)(&Ks[buf][(16 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + 4 * j * rs2 + (voff - 16 * wave * rs2),
+        __builtin_amdgcn_global_load_lds(vt + 4 * j * rs2 + (voff + 16 * (lchunk ^ ((lrow << 1) | ((j >> 1) << 3)))),
                                          (lds_void *)(&Vs[buf][(16 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
       }
       return;
@@ -212,12 +221,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     for (int j = 0; j < 4; ++j) {
       const int R = 16 * wave + 4 * j + lrow;
       const int kj = min(key0 + k_row_key(R), a.T - 1);
-      const int kc = lchunk ^ (R & 7);
+      const int kc = lchunk ^ (R & 15);
       __builtin_amdgcn_global_load_lds(kbase + kj * rstride + 8 * kc,
                                        (lds_void *)(&Ks[buf][(16 * wave + 4 * j) * kRowBytes]),
                                        16, 0, 0);
       const int vj = min(key0 + R, a.T - 1);
-      const int vc = lchunk ^ ((R & 3) << 1);
+      const int vc = lchunk ^ v_swz(R);
       __builtin_amdgcn_global_load_lds(vbase + vj * rstride + 8 * vc,
                                        (lds_void *)(&Vs[buf][(16 * wave + 4 * j) * kRowBytes]),
                                        16, 0, 0);
@@ -265,17 +274,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   __syncthreads();                // ... and everyone else's
 
   // Per-lane V^T transpose-read addresses: source lane s = lr of group lg points
-  // at key 8*lg + s/4 of the half (+4 for hi), dims 16*db + 4*(s%4); am[m]
-  // covers dims blocks db = m and m + 4 of Vs[0] (v_byte with the swizzle
-  // term folded in).
-  uint32_t am[4];
+  // at key 8*lg + s/4 of the half (+4 for hi), dims 16*db + 4*(s%4); am[db] is
+  // that address for dims block db in the first half of Vs[0] (v_byte with the
+  // swizzle folded in; g is the same for the row 4 further down).
+  uint32_t am[8];
   {
     const int vrow0 = 8 * lg + lr / 4;
-    const int vs = vrow0 & 3;
+    const int gs = v_swz(vrow0) >> 1;
     const uint32_t vbase0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Vs[0][0])));
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      am[m] = vbase0 + vrow0 * kRowBytes + 32 * (m ^ vs) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+    for (int db = 0; db < 8; ++db)
+      am[db] = vbase0 + vrow0 * kRowBytes + 32 * (db ^ gs) + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
   }
 
   // One tile of 64 keys. kMask: apply the causal (and key-valid) mask; tiles
@@ -290,9 +299,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       issue_tile(key0 + kBN, buf ^ 1);
       load_valid(key0 + kBN);
     }
-    uint32_t amb[4];
+    uint32_t amb[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) amb[m] = am[m] + buf * kTileBytes;
+    for (int db = 0; db < 8; ++db) amb[db] = am[db] + buf * kTileBytes;
 
     auto half = [&](auto hconst) {
       constexpr int h = decltype(hconst)::value;
@@ -423,7 +432,7 @@ int pick_gc(int G) {
 
 }  // namespace
 
-bool prefill_mfma_supported(int Hq, int Hkv, int D, int dtype) {
+bool prefill_mfma_supported(int64_t kv_rows, int Hq, int Hkv, int D, int dtype) {
   return dtype == GROK_BF16 && D == kD && Hkv > 0 && Hq % Hkv == 0;
 }
 
