@@ -12,7 +12,8 @@
 //   Y^T[n, m] = sum_k W^T[n, k] X^T[k, m]     A = W^T (LDS, k-contiguous)
 //                                             B = X   (LDS, k-contiguous)
 // Workgroup tile 128 (n) x 128 (m), K step 64, 4 waves in 2 x 2, each wave
-// 64 x 64 = 4 x 4 MFMA tiles; LDS double-buffered.
+// 64 x 64 = 4 x 4 MFMA tiles. X tiles triple-buffered in LDS (requested two
+// steps ahead), W^T tiles double-buffered (one step ahead, via registers).
 #include "common.h"
 
 namespace grok {
@@ -39,17 +40,54 @@ __device__ __forceinline__ float i8_to_f32(uint32_t word, int byte) {
 }
 
 // LDS layout of both tiles (X rows m, W^T rows n; 64 k values = 128 bytes per
-// row): 16-byte chunk c of row r sits at chunk c ^ sw(r). Two rows share one
-// 256-byte line of the 64 four-byte banks; the swizzle spreads the 16 rows of a
-// fragment read over all 16 chunk positions of a line pair and keeps the
-// transposed W^T stores at two lanes per position.
-__device__ __forceinline__ int sw(int r) { return (r ^ (r >> 3)) & 7; }
+// row): 16-byte chunk c of row r sits at chunk c ^ sw(r). This swizzle was
+// chosen by measurement (SQ_LDS_BANK_CONFLICT on isolated access patterns):
+// it is conflict-free both for the fragment reads (16 consecutive rows, one
+// chunk) and for the transposed W^T stores (rows 4*g + j over 32 lanes g).
+__device__ __forceinline__ int sw(int r) { return (r ^ (r >> 2)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kRowB + ((c ^ sw(r)) << 4); }
+
+// Fragment reads as inline assembly: the compiler cannot tell them apart from
+// the X tiles still streaming into other LDS buffers and would wait for those
+// loads first. LDS operations complete in order; results are used only after
+// lds_wait, which passes them through.
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+template <int kOff>
+__device__ __forceinline__ bf16x8 lds_read_b128_at(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff) : "memory");
+  return r;
+}
+// The 8 fragment reads of k-step kk: blocks b = 0..3 of 16 rows at byte
+// 16*b*128 from the base for q = kk ^ (b % 2).
+template <int kKK>
+__device__ __forceinline__ void read_frags(bf16x8 (&bx)[4], bf16x8 (&aw)[4], const uint32_t (&xq)[2],
+                                           const uint32_t (&wq)[2]) {
+  bx[0] = lds_read_b128_at<0 * 2048>(xq[kKK ^ 0]);
+  bx[1] = lds_read_b128_at<1 * 2048>(xq[kKK ^ 1]);
+  bx[2] = lds_read_b128_at<2 * 2048>(xq[kKK ^ 0]);
+  bx[3] = lds_read_b128_at<3 * 2048>(xq[kKK ^ 1]);
+  aw[0] = lds_read_b128_at<0 * 2048>(wq[kKK ^ 0]);
+  aw[1] = lds_read_b128_at<1 * 2048>(wq[kKK ^ 1]);
+  aw[2] = lds_read_b128_at<2 * 2048>(wq[kKK ^ 0]);
+  aw[3] = lds_read_b128_at<3 * 2048>(wq[kKK ^ 1]);
+}
+
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+               : "i"(kLeft));
+}
 
 __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
     const bf16_t *__restrict__ x, const int8_t *__restrict__ w, const float *__restrict__ scales,
     bf16_t *__restrict__ y, int64_t M, int K, int N) {
-  __shared__ __attribute__((aligned(1024))) unsigned char Xs[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Xs[3][kTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char Wt[2][kTileB];
 
   const int tid = threadIdx.x;
@@ -66,7 +104,23 @@ __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
   // (L%8) ^ sw(row). Rows past M read row M-1 and columns past K read the last
   // 8 columns (finite values; the matching W^T entries are zero).
   const int xl_row = lane / 8, xl_pos = lane % 8;
+  // Fast path: byte offsets from the tile's first element, fixed per lane
+  // (rows already clamped to M-1); slow path only for a K tail.
+  uint32_t xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + xl_row;
+    xoff[i] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2) + 16 * (xl_pos ^ sw(r));
+  }
+  const char *xtile = reinterpret_cast<const char *>(x + m0 * K);
   auto issue_x = [&](int k0, int buf) {
+    if (k0 + kBK <= K) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(xtile + 2 * k0 + xoff[i],
+                                         (lds_void *)(&Xs[buf][(32 * wave + 8 * i) * kRowB]), 16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 32 * wave + 8 * i + xl_row;
@@ -77,29 +131,69 @@ __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
     }
   };
 
-  // W staging: 4 rows (k) x 8 channels (n) int8 per thread, widened to bf16 and
-  // stored transposed (8 rows of W^T, 4 k values = 8 bytes each).
-  const int wnc = tid % 16, wkq = tid / 16;  // channels 8*wnc.., k rows 4*wkq..
-  u32x2 wr[4];
+  // W staging: 8 rows (k) x 4 channels (n) int8 per thread (one 4-byte load
+  // per k row; 32 lanes cover 128 contiguous channels), widened to bf16 and
+  // stored transposed: channel j's 8 k values are one 16-byte chunk of W^T row
+  // 4*wg + j. The loads are inline assembly so that the compiler does not add
+  // its own wait for them (it cannot count them against the X tile loads); the
+  // loop waits explicitly. Entries past K or N read a clamped address and are
+  // zeroed after the wait (wvalid).
+  const int wg = tid % 32, wkc = tid / 32;  // channels 4*wg.., k rows 8*wkc..
+  uint32_t wr[8];
+  uint32_t wvalid = 0;
+  const uint32_t woff = static_cast<uint32_t>(8 * wkc) * N + 4 * wg;  // byte offset in a k-step tile
+  const bool w_full_n = n0 + kBN <= N;
   auto gload_w = [&](int k0) {
-    const int n = n0 + 8 * wnc;
+    if (w_full_n && k0 + kBK <= K) {
+      wvalid = 0xffu;
+      const int8_t *wt = w + static_cast<int64_t>(k0) * N + n0;  // wave-uniform
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int k = k0 + 4 * wkq + r;
-      wr[r] = (k < K && n < N) ? *reinterpret_cast<const u32x2 *>(w + static_cast<int64_t>(k) * N + n) : u32x2{0, 0};
+      for (int r = 0; r < 8; ++r)
+        asm volatile("global_load_dword %0, %1, %2" : "=v"(wr[r]) : "v"(woff + r * N), "s"(wt) : "memory");
+      return;
+    }
+    const int n = n0 + 4 * wg;
+    wvalid = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int k = k0 + 8 * wkc + r;
+      const bool ok = k < K && n < N;
+      wvalid |= ok ? (1u << r) : 0u;
+      const int8_t *src = w + static_cast<int64_t>(ok ? k : 0) * N + (ok ? n : 0);
+      asm volatile("global_load_dword %0, %1, off" : "=v"(wr[r]) : "v"(src) : "memory");
     }
   };
   auto lstore_w = [&](int buf) {
+    if (wvalid != 0xffu) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int wd = j / 4, by = j % 4;
-      const float f0 = i8_to_f32(wr[0][wd], by), f1 = i8_to_f32(wr[1][wd], by);
-      const float f2 = i8_to_f32(wr[2][wd], by), f3 = i8_to_f32(wr[3][wd], by);
-      const u32x2 pk = {cvt_pk_bf16(f0, f1), cvt_pk_bf16(f2, f3)};
-      const int n = 8 * wnc + j;
-      *reinterpret_cast<u32x2 *>(&Wt[buf][lds_off(n, wkq >> 1) + 8 * (wkq & 1)]) = pk;
+      for (int r = 0; r < 8; ++r)
+        if (!(wvalid & (1u << r))) wr[r] = 0;
+    }
+    const uint32_t wt0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Wt[buf][0])));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 pk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pk[q] = cvt_pk_bf16(i8_to_f32(wr[2 * q], j), i8_to_f32(wr[2 * q + 1], j));
+      const uint32_t a = wt0 + lds_off(4 * wg + j, wkc);
+      asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(pk) : "memory");
     }
   };
+
+  // Fragment read addresses. For row R0 + lr (R0 = 16 * block, a multiple of
+  // 16) and chunk 4*kk + lg, lds_off = R0*128 + lr*128 + 16*((lg ^ s) ^ 4*q)
+  // with s = (lr % 8) ^ (lr / 4) and q = kk ^ (block % 2): two per-lane bases
+  // (q = 0, 1) plus immediates cover every fragment read of a step.
+  uint32_t xrd[2], wrd[2];
+  {
+    const int sl = (lr & 7) ^ (lr >> 2);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t a = lr * kRowB + 16 * ((lg ^ sl) ^ (4 * q));
+      xrd[q] = 64 * wm * kRowB + a;
+      wrd[q] = 64 * wn * kRowB + a;
+    }
+  }
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -107,37 +201,63 @@ __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Pipeline: the X tile of step t+2 is requested while step t computes (three
+  // X buffers), the W tile of step t+1 one step ahead (two W buffers). The
+  // loads of a step are issued W first, then X, so the wait at the end of step
+  // t (W of t+1 and X of t+1 complete) leaves the four X(t+2) loads in flight.
   const int nk = (K + kBK - 1) / kBK;
-  issue_x(0, 0);
   gload_w(0);
+  issue_x(0, 0);
+  issue_x(min(1, nk - 1) * kBK, 1);
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(wr[0]), "+v"(wr[1]), "+v"(wr[2]), "+v"(wr[3]), "+v"(wr[4]),
+               "+v"(wr[5]), "+v"(wr[6]), "+v"(wr[7]) : : "memory");
   lstore_w(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     const int buf = t & 1;
+    const int xbuf = t % 3;
     const bool more = t + 1 < nk;
-    if (more) {
-      issue_x((t + 1) * kBK, buf ^ 1);
-      gload_w((t + 1) * kBK);
-    }
+    // Issued unconditionally (clamped at the end) so that every step has the
+    // same number of loads in flight: W(t+1), then X(t+2).
+    gload_w(min(t + 1, nk - 1) * kBK);
+    issue_x(min(t + 2, nk - 1) * kBK, (t + 2) % 3);
+    const uint32_t xb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Xs[xbuf][0])));
+    const uint32_t wb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Wt[buf][0])));
+    const uint32_t xq[2] = {xb + xrd[0], xb + xrd[1]};
+    const uint32_t wq[2] = {wb + wrd[0], wb + wrd[1]};
+    bf16x8 bx[2][4], aw[2][4];
+    read_frags<0>(bx[0], aw[0], xq, wq);
+    read_frags<1>(bx[1], aw[1], xq, wq);
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
-      bf16x8 bx[4];
+      if (kk == 0) {
+        lds_wait<8>(bx[0], aw[0]);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait<0>(bx[1], aw[1]);
+      }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        bx[mb] = *reinterpret_cast<const bf16x8 *>(&Xs[buf][lds_off(64 * wm + 16 * mb + lr, 4 * kk + lg)]);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(&Wt[buf][lds_off(64 * wn + 16 * nb + lr, 4 * kk + lg)]);
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bx[mb], acc[nb][mb], 0, 0, 0);
-      }
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[kk][nb], bx[kk][mb], acc[nb][mb], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the waits below stay after this step's MFMAs
+    // W(t+1) and X(t+1) have landed once at most the 4 X(t+2) loads remain.
+    asm volatile("s_waitcnt vmcnt(4)" : "+v"(wr[0]), "+v"(wr[1]), "+v"(wr[2]), "+v"(wr[3]), "+v"(wr[4]),
+                 "+v"(wr[5]), "+v"(wr[6]), "+v"(wr[7]) : : "memory");
     if (more) lstore_w(buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's X loads for the next step have landed
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // LDS stores done
+    // Workgroup barrier without a memory fence (a fence would wait for the X
+    // loads still in flight); the asm memory clobber keeps LDS accesses on
+    // their side of it.
+    asm volatile("s_barrier" ::: "memory");
   }
+
+  // The last steps re-requested tiles they do not use: let those LDS-bound
+  // loads land before the workgroup can exit and release its LDS.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Epilogue: lane holds Y^T[n = nbase + 4*lg + v, m = mbase + lr], v = 0..3.
 #pragma unroll
