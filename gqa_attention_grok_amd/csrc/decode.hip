@@ -8,43 +8,35 @@
 // HBM-bound: every valid K/V row (256 B each) is read exactly once and slots at
 // or beyond kv_len are never touched.
 //
-// Kernel 1 (decode_split_kernel): one workgroup per (sequence, split of
-// `split_keys` cache slots, group of up to 8 KV heads), one wave per KV head.
-// The cache stores the 8 KV heads of a slot side by side (2 KB), so the waves
-// of a workgroup together stream whole contiguous slot rows. Each wave walks
-// its split in tiles of 32 keys, loading tile t+1 while it computes tile t.
-// MFMA rows are the G <= 16 query heads of the wave's KV head (unused rows are
-// zero):
-//   S^T[key, head] = K . Q^T   (K fragments loaded straight from HBM)
-//   O^T[d, head]  += V^T . P^T (V transposed through the wave's own LDS slice)
-// The softmax uses the fixed shift exp(c - cap): unmasked softcapped logits lie
-// in [-cap, cap], so a split's partial result is a plain pair of sums
-// (sum p*v, sum p) with no running maximum to reconcile.
+// Kernel 1 (decode_split_kernel): one workgroup of 4 waves per (sequence, KV
+// head, split of 128 cache slots). The whole split -- 128 K rows and 128 V
+// rows of the head, 64 KB -- is requested up front: K straight into the
+// registers that feed the MFMA (each lane loads its own fragments), V HBM ->
+// LDS (global_load_lds) for the transpose reads. With 32 KB of LDS per
+// workgroup, three workgroups per CU keep up to 192 KB in flight and overlap
+// one's loads with another's compute. Wave w owns slots 32w .. 32w+31 of the
+// split: it loads them itself (no barrier before the compute) and runs, with
+// the G <= 16 query heads of the KV head as MFMA rows (unused rows zero),
+//   S^T[slot, head] = K . Q^T    (slot rows permuted as in the prefill K tile)
+//   O^T[d, head]  += V^T . P^T   (V^T from LDS transpose reads)
+// using the tile layouts of the prefill kernel. The softmax uses the fixed shift
+// exp(c - cap): unmasked softcapped logits lie in [-cap, cap], so partial
+// results are plain sums (sum p*v, sum p) with no running maximum to
+// reconcile. The four waves' partials are added in LDS and one partial per
+// split is written.
 // Kernel 2 (decode_combine_kernel): one workgroup per (sequence, query head)
 // adds the partials of the splits and writes bf16 sum(p*v) / sum(p).
-#include "common.h"
+#include "attn_tile.h"
 
 namespace grok {
 namespace {
 
+using namespace attn;
+
 constexpr int kD = 128;
-constexpr int kWavesMax = 8;  // KV heads per workgroup
-constexpr int kTile = 32;
-// V^T slice of a wave: 128 rows (dims) of 32 keys (64 B, four 16-byte groups of
-// 8 keys). The group of key k in row d is stored at (k/8) ^ ((d/2) % 4), which
-// spreads the 16-byte fragment reads of 8 consecutive rows over all banks.
-__device__ __forceinline__ int vt_index(int d, int k) {
-  return d * kTile + ((((k >> 3) ^ (d >> 1)) & 3) << 3) + (k & 7);
-}
+constexpr int kSplit = 128;  // cache slots per workgroup
+constexpr int kSplitWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  f32x2 f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-}
 
 struct DecodeArgs {
   const bf16_t *q, *kc, *vc;
@@ -54,138 +46,148 @@ struct DecodeArgs {
   float *part_l;  // [B, Hkv, S, G]
   int32_t *status;
   int B, Tmax, Hq, Hkv, G, S, split_keys;
-  float k1, k2;
+  float k1, k2inv;
 };
 
-// One tile's operands in registers: K fragments (A operand of S^T, rows
-// permuted so that accumulator slot v of lane l is key 8*lg + 4*kb + v) and two
-// (4-key quad, 8-dim chunk) slices of V.
-struct TileRegs {
-  u32x4 k[2][4];
-  u32x4 v[2][4];
-};
+__global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[kSplit * kRowBytes];
+  __shared__ float red_l[kSplitWaves][16];
 
-__device__ __forceinline__ void load_tile(TileRegs &r, const bf16_t *kbase, const bf16_t *vbase,
-                                          int64_t rstride, int key0, int len, int lane) {
-  const int lr = lane % 16, lg = lane / 16;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int j = key0 + 8 * (lr / 4) + 4 * kb + (lr % 4);
-    const bool ok = j < len;
-    const bf16_t *kp = kbase + (ok ? j : 0) * rstride + 8 * lg;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      r.k[kb][kk] = ok ? *reinterpret_cast<const u32x4 *>(kp + 32 * kk) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int item = lane + kWave * it;
-    const int kq = item % 8, vc = item / 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = key0 + 4 * kq + i;
-      r.v[it][i] = j < len ? *reinterpret_cast<const u32x4 *>(vbase + j * rstride + 8 * vc) : u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-__global__ __launch_bounds__(kWavesMax * kWave) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kWavesMax][kD * kTile];
-
-  const int b = blockIdx.z, s = blockIdx.x;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int g = blockIdx.y * kWavesMax + wave;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int len = a.kv_len[b];
   if (len < 1 || len > a.Tmax) return;  // reported by the combine kernel
-  const int sbase = s * a.split_keys;
-  if (sbase >= len || g >= a.Hkv) return;  // no barrier below: waves may leave
+  const int sbase = s * kSplit;
+  if (sbase >= len) return;  // whole workgroup: no barrier is skipped
 
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lr = lane % 16, lg = lane / 16;
+  const int last = len - 1;
+
+  // Q fragment: head row lr (zero beyond G), dims 32*kk + 8*lg; then this
+  // wave's 32 K slots: the S^T A operand of key block kb is, for lane
+  // (lr, lg), slot 32*wave + k_row_key(16*kb + lr) of the split, dims
+  // 32*kk + 8*lg .. +8. Both go straight into registers; then the V slots,
+  // HBM -> LDS: instruction j (0..7) fills LDS rows R = 32*wave + 4*j + L/16
+  // (slot R), lane L writing physical chunk L%16. Slots past the sequence read
+  // its last slot (masked below). The register loads are inline assembly and
+  // issued first, so one explicit wait (vmcnt(8)) makes Q and K usable while
+  // the eight V loads stay in flight.
   const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
   const bf16_t *kbase = a.kc + (static_cast<int64_t>(b) * a.Tmax * a.Hkv + g) * kD;
   const bf16_t *vbase = a.vc + (static_cast<int64_t>(b) * a.Tmax * a.Hkv + g) * kD;
-  const int send = min(len, sbase + a.split_keys);
-
-  TileRegs cur, nxt;
-  load_tile(cur, kbase, vbase, rstride, sbase, send, lane);
-
-  // Q fragment: head row lr (zero beyond G), dims 32*kk + 8*lg.
-  bf16x8 qf[4];
+  const bool qok = lr < a.G;
+  u32x4 qw[4], kf[2][4];
   {
-    const bool ok = lr < a.G;
-    const bf16_t *qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (ok ? lr : 0)) * kD;
+    const bf16_t *qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (qok ? lr : 0)) * kD;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 w = ok ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * lg) : u32x4{0, 0, 0, 0};
-      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    for (int kk = 0; kk < 4; ++kk) asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qw[kk]) : "v"(qp + 32 * kk + 8 * lg) : "memory");
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kj = min(sbase + 32 * wave + k_row_key(16 * kb + lr), last);
+    const bf16_t *kp = kbase + kj * rstride + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kf[kb][kk]) : "v"(kp + 32 * kk) : "memory");
+  }
+  {
+    const int lrow = lane / 16, lchunk = lane % 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int R = 32 * wave + 4 * j + lrow;
+      const int vj = min(sbase + R, last);
+      __builtin_amdgcn_global_load_lds(vbase + vj * rstride + 8 * (lchunk ^ v_swz(R)),
+                                       (lds_void *)(&Vs[(32 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
     }
   }
 
-  f32x4 oacc[8];
+  asm volatile("s_waitcnt vmcnt(8)"
+               : "+v"(qw[0]), "+v"(qw[1]), "+v"(qw[2]), "+v"(qw[3]), "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(kf[0][2]),
+                 "+v"(kf[0][3]), "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(kf[1][2]), "+v"(kf[1][3])
+               :
+               : "memory");
+  bf16x8 qf[4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, qok ? qw[kk] : u32x4{0, 0, 0, 0});
+
+  // S^T for the wave's 32 slots; accumulator slot v of lane l is slot
+  // 32*wave + 8*lg + 4*kb + v of the split.
+  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kb][kk]), qf[kk], sacc[kb],
+                                                         0, 0, 0);
+  // p = exp2(k2 / (1 + exp2(k1*s))), masked past the sequence; bf16 for P.V.
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float ex = __builtin_amdgcn_exp2f(sacc[e >> 2][e & 3] * a.k1);
+    const float pv = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(__builtin_fmaf(ex, a.k2inv, a.k2inv)));
+    p[e] = (sbase + 32 * wave + 8 * lg + e <= last) ? pv : 0.f;
+  }
+  const u32x4 pw = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                    cvt_pk_bf16(p[6], p[7])};
+  // Row sum of the bf16-rounded weights that P.V uses.
   float lsum = 0.f;
-
-  for (int key0 = sbase; key0 < send; key0 += kTile) {
-    const int next0 = key0 + kTile;
-    if (next0 < send) load_tile(nxt, kbase, vbase, rstride, next0, send, lane);
-
-    // V^T of this tile into the wave's own LDS slice: 4 keys per 8-byte write.
-    // LDS operations of one wave complete in order, so the fragment reads below
-    // see these writes and the next tile's writes follow this tile's reads.
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = lane + kWave * it;
-      const int kq = item % 8, vc = item / 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint32_t x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (e & 1) ? (cur.v[it][i][wd] >> 16) : (cur.v[it][i][wd] & 0xffffu);
-        const u32x2 w = {x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
-        *reinterpret_cast<u32x2 *>(&Vt[wave][vt_index(8 * vc + e, 4 * kq)]) = w;
-      }
-    }
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kb][kk]), qf[kk],
-                                                           sacc[kb], 0, 0, 0);
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float sv = sacc[e >> 2][e & 3];
-      const float ex = __builtin_amdgcn_exp2f(sv * a.k1);
-      const float r = __builtin_amdgcn_rcpf(1.f + ex);
-      const float pv = __builtin_amdgcn_exp2f(a.k2 * r);
-      p[e] = (key0 + 8 * lg + e < send) ? pv : 0.f;
-    }
-    const u32x4 pw = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
-                      cvt_pk_bf16(p[6], p[7])};
-    // Row sum of the bf16-rounded weights that P.V uses.
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lsum += lo_bf16(pw[e]) + hi_bf16(pw[e]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[wave][vt_index(16 * db + lr, 8 * lg)]);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[db], 0, 0, 0);
-    }
-    cur = nxt;
-  }
+  for (int e = 0; e < 4; ++e) lsum = add_bf16_pair(lsum, pw[e]);
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
 
-  // This wave's partial: O^T lane l holds head row lr, dims 16*db + 4*lg + v.
-  const int64_t pbase = ((static_cast<int64_t>(b) * a.Hkv + g) * a.S + s) * a.G;
-  if (lr < a.G) {
-    float *po = a.part_o + (pbase + lr) * kD;
+  // This wave's V slots have landed (it reads only those). The softmax results
+  // pass through the wait so that it is not hoisted above the softmax.
+  u32x4 pw2 = pw;
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(pw2), "+v"(lsum) : : "memory");
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, pw2);
+
+  // O^T += V^T . P^T: lane l's V^T fragment (dim 16*db + lr, slots 8*lg .. +7
+  // of the wave's 32) from two transpose reads of 4 slots.
+  f32x4 oacc[8];
+  {
+    const int vrow0 = 32 * wave + 8 * lg + lr / 4;
+    const int gs = v_swz(vrow0) >> 1;
+    const uint32_t vb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Vs[0]))) +
+                        vrow0 * kRowBytes + 16 * ((lr & 3) >> 1) + 8 * (lr & 1);
+    u32x2 lo[8], hi[8];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * lg) = oacc[db];
-    if (lg == 0) a.part_l[pbase + lr] = lsum;
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t ad = vb + 32 * (db ^ gs);
+      lo[db] = lds_read_tr16<0>(ad);
+      hi[db] = lds_read_tr16<4 * kRowBytes>(ad);
+    }
+    lds_wait<8>(lo, hi);
+    lds_wait<0>(lo + 4, hi + 4);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[db][0], lo[db][1], hi[db][0], hi[db][1]});
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+  }
+
+  // Add the four waves' partials (lane l: head row lr, dims 16*db + 4*lg + v)
+  // in LDS, reusing the V tile, and write this split's partial.
+  __syncthreads();  // every wave is done with Vs
+  float *red_o = reinterpret_cast<float *>(Vs);  // [4][16][128]
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<f32x4 *>(&red_o[(wave * 16 + lr) * kD + 16 * db + 4 * lg]) = oacc[db];
+  if (lg == 0) red_l[wave][lr] = lsum;
+  __syncthreads();
+  const int64_t pbase = ((static_cast<int64_t>(b) * a.Hkv + g) * a.S + s) * a.G;
+  for (int it = threadIdx.x; it < a.G * (kD / 4); it += kSplitWaves * kWave) {
+    const int row = it / (kD / 4), c4 = it % (kD / 4);
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) o += *reinterpret_cast<const f32x4 *>(&red_o[(w * 16 + row) * kD + 4 * c4]);
+    *reinterpret_cast<f32x4 *>(a.part_o + (pbase + row) * kD + 4 * c4) = o;
+  }
+  if (threadIdx.x < a.G) {
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) l += red_l[w][threadIdx.x];
+    a.part_l[pbase + threadIdx.x] = l;
   }
 }
 
@@ -249,19 +251,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
   }
 }
 
-// Keys per split: long splits amortise the partial sums, short ones give a
-// small batch enough workgroups to cover the 256 compute units.
-int split_keys_for(int B, int Tmax, int Hkv) {
-  const int groups = (Hkv + kWavesMax - 1) / kWavesMax;
-  const int64_t wgs_long = static_cast<int64_t>(B) * groups * ((Tmax + 127) / 128);
-  return wgs_long >= 1024 ? 128 : 32;
-}
-
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv) {
-  const int sk = split_keys_for(B, Tmax, Hkv);
-  const size_t S = (static_cast<size_t>(Tmax) + sk - 1) / sk;
+  const size_t S = (static_cast<size_t>(Tmax) + kSplit - 1) / kSplit;
   const size_t G = static_cast<size_t>(Hq / Hkv);
   const size_t n = static_cast<size_t>(B) * Hkv * S * G;
   return n * kD * sizeof(float) + n * sizeof(float);
@@ -281,17 +274,15 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = Hq / Hkv;
-  a.split_keys = split_keys_for(B, Tmax, Hkv);
-  a.S = (Tmax + a.split_keys - 1) / a.split_keys;
+  a.split_keys = kSplit;
+  a.S = (Tmax + kSplit - 1) / kSplit;
   const size_t n = static_cast<size_t>(B) * Hkv * a.S * a.G;
   a.part_o = static_cast<float *>(ws);
   a.part_l = a.part_o + n * kD;
   a.status = status;
   a.k1 = 2.f * mult * kLog2e / cap;
-  a.k2 = -2.f * cap * kLog2e;
-  const int groups = (Hkv + kWavesMax - 1) / kWavesMax;
-  const int waves = Hkv < kWavesMax ? Hkv : kWavesMax;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.S, groups, B), dim3(waves * kWave), 0, st, a);
+  a.k2inv = 1.f / (-2.f * cap * kLog2e);
+  hipLaunchKernelGGL(decode_split_kernel, dim3(a.S, Hkv, B), dim3(kSplitWaves * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);

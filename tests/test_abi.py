@@ -134,10 +134,12 @@ def test_decode_validation_and_workspace(lib):
     ws = lib.grok_attn_decode_workspace_bytes
     ws.restype = ctypes.c_size_t
     n = ws(i(1), i(8192), i(48), i(8), i(128))
-    # one sequence: 256 splits of 32 slots x 8 KV heads x 6 heads x (128 + 1) floats
-    assert n == 256 * 8 * 6 * 129 * 4
-    # 32 sequences: 64 splits of 128 slots
+    # one sequence: 64 splits of 128 slots x 8 KV heads x 6 heads x (128 + 1) floats
+    assert n == 64 * 8 * 6 * 129 * 4
+    # 32 sequences
     assert ws(i(32), i(8192), i(48), i(8), i(128)) == 32 * 64 * 8 * 6 * 129 * 4
+    # a ragged capacity rounds the split count up
+    assert ws(i(2), i(1000), i(48), i(8), i(128)) == 2 * 8 * 8 * 6 * 129 * 4
     assert ws(i(1), i(8192), i(48), i(8), i(64)) == 0
     assert ws(i(1), i(8192), i(47), i(8), i(128)) == 0
 
