@@ -211,7 +211,9 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
   const int ns = (len + a.split_keys - 1) / a.split_keys;
   const int c = threadIdx.x % (kD / 4), sg = threadIdx.x / (kD / 4);
   const int64_t base = (static_cast<int64_t>(b) * a.Hkv + g) * a.S;
-  // 4 independent partial sums per thread keep 4 loads in flight.
+  // Up to 8 partials per thread per round, all loads issued before any sum, so
+  // a round costs one memory latency (one round covers 64 splits = 8192 slots).
+  constexpr int kU = 8;
   f32x4 acc[4];
   float l[4];
 #pragma unroll
@@ -219,19 +221,23 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     l[u] = 0.f;
   }
-  int sp = sg;
-  for (; sp + 3 * kSplitGroups < ns; sp += 4 * kSplitGroups) {
+  for (int sp0 = sg; sp0 < ns; sp0 += kU * kSplitGroups) {
+    f32x4 vo[kU];
+    float vl[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t row = (base + sp + u * kSplitGroups) * a.G + hh;
-      acc[u] += *reinterpret_cast<const f32x4 *>(a.part_o + row * kD + 4 * c);
-      l[u] += a.part_l[row];
+    for (int u = 0; u < kU; ++u) {
+      const int sp = sp0 + u * kSplitGroups;
+      const int64_t row = (base + (sp < ns ? sp : 0)) * a.G + hh;
+      vo[u] = *reinterpret_cast<const f32x4 *>(a.part_o + row * kD + 4 * c);
+      vl[u] = a.part_l[row];
     }
-  }
-  for (; sp < ns; sp += kSplitGroups) {
-    const int64_t row = (base + sp) * a.G + hh;
-    acc[0] += *reinterpret_cast<const f32x4 *>(a.part_o + row * kD + 4 * c);
-    l[0] += a.part_l[row];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (sp0 + u * kSplitGroups < ns) {
+        acc[u % 4] += vo[u];
+        l[u % 4] += vl[u];
+      }
+    }
   }
   acc[0] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   l[0] = (l[0] + l[1]) + (l[2] + l[3]);

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
   const int t = blockIdx.x % T_;
   const int s0 = step[b];
   const bool ok = s0 >= 0 && s0 <= Tmax - T_;
-  if (t == 0 && threadIdx.x == 0) {
+  if (t == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     if (new_step) new_step[b] = ok ? s0 + T_ : s0;
     if (!ok && status) *status = GROK_ERANGE;
   }
@@ -131,7 +131,10 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
   const int nv = Hkv * (D / 8);
   const int64_t tok = static_cast<int64_t>(b) * T_ + t;
   const int64_t slot = static_cast<int64_t>(b) * Tmax + pos;
-  for (int w = threadIdx.x; w < nq + nk + nv; w += kThreads) {
+  // One work item (a q or k chunk pair to rotate, or a 16-byte piece of v)
+  // per thread: the token's items are spread over gridDim.y workgroups so that
+  // all loads are in flight at once.
+  for (int w = blockIdx.y * kThreads + threadIdx.x; w < nq + nk + nv; w += kThreads * gridDim.y) {
     if (w < nq + nk) {
       const int ww = w < nq ? w : w - nq;
       const int h = ww / nchunk, c = ww % nchunk;
@@ -193,7 +196,9 @@ hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, 
                       reinterpret_cast<uintptr_t>(kn) | reinterpret_cast<uintptr_t>(vn) |
                       reinterpret_cast<uintptr_t>(q);
   if (a % 16 != 0 || D % 16 != 0) return hipErrorInvalidValue;  // validated by the caller
-  hipLaunchKernelGGL((kv_append_kernel<8>), dim3(B * T), dim3(kThreads), 0, s,
+  const int items = (q ? Hq * (D / 2 / 8) : 0) + Hkv * (D / 2 / 8) + Hkv * (D / 8);
+  const int wgs_per_token = (items + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((kv_append_kernel<8>), dim3(B * T, wgs_per_token), dim3(kThreads), 0, s,
                      static_cast<bf16_t *>(kc), static_cast<bf16_t *>(vc),
                      static_cast<const bf16_t *>(kn), static_cast<const bf16_t *>(vn),
                      static_cast<bf16_t *>(q), step, new_step, status, T, Tmax, Hq, Hkv, D,

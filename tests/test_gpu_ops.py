@@ -295,6 +295,7 @@ def test_prefill_generic(G, B, T, Hq, Hkv, D, dtype, padded):
     (48, 8, [1, 127, 128, 129, 1024], 1024),
     (16, 1, [33, 300], 512),
     (8, 8, [5, 256], 256),
+    (6, 3, [200, 77, 1], 200),  # capacity not a multiple of the 128-slot split
 ])
 def test_decode(G, Hq, Hkv, lens, Tmax):
     grok, U, torch = G
