@@ -11,20 +11,24 @@
 // epilogue writes runs of 4 consecutive output channels:
 //   Y^T[n, m] = sum_k W^T[n, k] X^T[k, m]     A = W^T (LDS, k-contiguous)
 //                                             B = X   (LDS, k-contiguous)
-// Workgroup tile 128 (n) x 128 (m), K step 64, 4 waves in 2 x 2, each wave
-// 64 x 64 = 4 x 4 MFMA tiles. X tiles triple-buffered in LDS (requested two
-// steps ahead), W^T tiles double-buffered (one step ahead, via registers).
+// Workgroup tile 128 (n) x 256 (m), K step 64, 8 waves in 4 (m) x 2 (n), each
+// wave 64 x 64 = 4 x 4 MFMA tiles; one workgroup per CU (128 KB of LDS). X
+// tiles triple-buffered in LDS (requested two steps ahead), W^T tiles
+// double-buffered (one step ahead, via registers; staged by waves 0-3, so the
+// int8 widening is paid once per 256 rows).
 #include "common.h"
 
 namespace grok {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kStageThreads = 256;  // threads that stage the W tile
 constexpr int kBN = 128;  // output channels per workgroup
-constexpr int kBM = 128;  // rows per workgroup
+constexpr int kBM = 256;  // rows per workgroup
 constexpr int kBK = 64;
 constexpr int kRowB = kBK * 2;  // one LDS row: 64 bf16 = 128 bytes, unpadded
-constexpr int kTileB = 128 * kRowB;
+constexpr int kTileB = 128 * kRowB;       // W^T tile: 128 rows
+constexpr int kXTileB = kBM * kRowB;      // X tile: 256 rows
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -84,10 +88,10 @@ __device__ __forceinline__ void lds_wait(bf16x8 (&a)[4], bf16x8 (&b)[4]) {
                : "i"(kLeft));
 }
 
-__global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
+__global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
     const bf16_t *__restrict__ x, const int8_t *__restrict__ w, const float *__restrict__ scales,
     bf16_t *__restrict__ y, int64_t M, int K, int N) {
-  __shared__ __attribute__((aligned(1024))) unsigned char Xs[3][kTileB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Xs[3][kXTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char Wt[2][kTileB];
 
   const int tid = threadIdx.x;
@@ -206,12 +210,13 @@ __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
   // loads of a step are issued W first, then X, so the wait at the end of step
   // t (W of t+1 and X of t+1 complete) leaves the four X(t+2) loads in flight.
   const int nk = (K + kBK - 1) / kBK;
-  gload_w(0);
+  const bool stager = wave < kStageThreads / kWave;  // wave-uniform
+  if (stager) gload_w(0);
   issue_x(0, 0);
   issue_x(min(1, nk - 1) * kBK, 1);
   asm volatile("s_waitcnt vmcnt(0)" : "+v"(wr[0]), "+v"(wr[1]), "+v"(wr[2]), "+v"(wr[3]), "+v"(wr[4]),
                "+v"(wr[5]), "+v"(wr[6]), "+v"(wr[7]) : : "memory");
-  lstore_w(0);
+  if (stager) lstore_w(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
     const bool more = t + 1 < nk;
     // Issued unconditionally (clamped at the end) so that every step has the
     // same number of loads in flight: W(t+1), then X(t+2).
-    gload_w(min(t + 1, nk - 1) * kBK);
+    if (stager) gload_w(min(t + 1, nk - 1) * kBK);
     issue_x(min(t + 2, nk - 1) * kBK, (t + 2) % 3);
     const uint32_t xb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Xs[xbuf][0])));
     const uint32_t wb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&Wt[buf][0])));
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_int8_kernel(
     // W(t+1) and X(t+1) have landed once at most the 4 X(t+2) loads remain.
     asm volatile("s_waitcnt vmcnt(4)" : "+v"(wr[0]), "+v"(wr[1]), "+v"(wr[2]), "+v"(wr[3]), "+v"(wr[4]),
                  "+v"(wr[5]), "+v"(wr[6]), "+v"(wr[7]) : : "memory");
-    if (more) lstore_w(buf ^ 1);
+    if (stager && more) lstore_w(buf ^ 1);
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // LDS stores done
     // Workgroup barrier without a memory fence (a fence would wait for the X
     // loads still in flight); the asm memory clobber keeps LDS accesses on
