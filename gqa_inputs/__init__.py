@@ -37,6 +37,7 @@ __all__ = [
     "make_prefill_inputs",
     "make_decode_inputs",
     "make_sublayer_inputs",
+    "make_decode_sublayer_inputs",
     "make_workload",
 ]
 
@@ -78,7 +79,7 @@ def int8_uniform(g: np.random.Generator, shape) -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "sublayer"
+    kind: str  # "prefill" | "decode" | "sublayer" | "decode_sublayer"
     seed: int
     dtype: str  # "f32" | "bf16"
     B: int
@@ -122,6 +123,14 @@ WORKLOADS = {
     "sublayer_b4_t2048": Workload(
         name="sublayer_b4_t2048", kind="sublayer", seed=1005, dtype="bf16",
         B=4, T=2048, Hq=48, Hkv=8, D=128, d_model=6144),
+    # Decode-time sub-layer: one new token against a full 8192-slot cache.
+    "decode_sublayer_b1_t8192": Workload(
+        name="decode_sublayer_b1_t8192", kind="decode_sublayer", seed=1006, dtype="bf16",
+        B=1, Hq=48, Hkv=8, D=128, Tmax=8192, d_model=6144),
+    # Decode-time sub-layer over 32 sequences of lengths uniform in [512, 8192].
+    "decode_sublayer_b32_t8192": Workload(
+        name="decode_sublayer_b32_t8192", kind="decode_sublayer", seed=1007, dtype="bf16",
+        B=32, Hq=48, Hkv=8, D=128, Tmax=8192, d_model=6144, ragged=True),
 }
 
 
@@ -185,6 +194,24 @@ def make_sublayer_inputs(B, T, d_model, Hq, Hkv, D, seed, scale=0.02 / 127,
             "sq": sc(Hq * D), "sk": sc(Hkv * D), "sv": sc(Hkv * D), "so": sc(d_model)}
 
 
+def make_decode_sublayer_inputs(B, d_model, Hq, Hkv, D, Tmax, seed, lengths=None, ragged=False,
+                                scale=0.02 / 127, distinct_scales=False):
+    """One new token per sequence: x [B,1,d] bf16, the int8 weights and scales
+    of ``make_sublayer_inputs``, and a cache [B,Tmax,Hkv,D] (every slot finite
+    N(0,1)) with step = length-1 (the new token's slot)."""
+    g = rng(seed)
+    k_cache = normal_bf16(g, (B, Tmax, Hkv, D))
+    v_cache = normal_bf16(g, (B, Tmax, Hkv, D))
+    if lengths is None:
+        lengths = g.integers(512, Tmax + 1, size=B) if ragged else np.full(B, Tmax)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    out = make_sublayer_inputs(B, 1, d_model, Hq, Hkv, D, int(g.integers(1 << 31)), scale,
+                               distinct_scales)
+    out.update({"k_cache": k_cache, "v_cache": v_cache, "step": (lengths - 1).astype(np.int32),
+                "kv_len": lengths.copy()})
+    return out
+
+
 def make_workload(name: str) -> dict:
     """All inputs of one named workload at its full size."""
     w = WORKLOADS[name]
@@ -192,4 +219,7 @@ def make_workload(name: str) -> dict:
         return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.seed, w.dtype)
     if w.kind == "decode":
         return make_decode_inputs(w.B, w.Hq, w.Hkv, w.D, w.Tmax, w.seed, ragged=w.ragged)
+    if w.kind == "decode_sublayer":
+        return make_decode_sublayer_inputs(w.B, w.d_model, w.Hq, w.Hkv, w.D, w.Tmax, w.seed,
+                                           ragged=w.ragged)
     return make_sublayer_inputs(w.B, w.T, w.d_model, w.Hq, w.Hkv, w.D, w.seed)

@@ -55,6 +55,7 @@ __all__ = [
     "attention_rows",
     "decode_step",
     "sublayer",
+    "decode_sublayer",
     "kv_cache_bytes",
 ]
 
@@ -317,6 +318,28 @@ def sublayer(x, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D, mult, cap=30.0,
     a = attention(q, k, v, mask, mult, cap, out=io)
     o = linear_int8(a, wo, so, out=io)
     return rmsnorm(o, None, eps, residual=x, out=io)
+
+
+def decode_sublayer(x, k_cache, v_cache, step, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D, mult,
+                    cap=30.0, eps=1e-5, base=10000.0, io="bf16"):
+    """Attention half of a decoder layer for one new token per sequence, with
+    KV memory ([ch6] §6.3.1 sandwich norm around [ch4] §4.5 attention; the
+    memory update of [ch4] §4.4 and [ch6] §6.6).
+
+    x [B, 1, d]; caches [B, Tmax, Hkv, D]; step [B] (the new token's slot and
+    position). n = norm(x); q, k, v = int8 projections of n; q and k roped at
+    step[b], k and v written to slot step[b]; attention over slots
+    [0, step[b] + 1); y = x + norm(Wo . attn). Each step's result is handed on
+    in the I/O dtype. Returns (y [B, 1, d], k_cache', v_cache', new_step).
+    """
+    B = x.shape[0]
+    n = rmsnorm(x, None, eps, out=io)
+    q = linear_int8(n, wq, sq, out=io).reshape(B, 1, Hq, D)
+    k = linear_int8(n, wk, sk, out=io).reshape(B, 1, Hkv, D)
+    v = linear_int8(n, wv, sv, out=io).reshape(B, 1, Hkv, D)
+    a, kc, vc, new_step = decode_step(k_cache, v_cache, q, k, v, step, mult, cap, base, io)
+    o = linear_int8(a, wo, so, out=io)
+    return rmsnorm(o, None, eps, residual=x, out=io), kc, vc, new_step
 
 
 def kv_cache_bytes(num_layers, batch, seq_len, num_kv_heads, head_size, elem_bytes=2):

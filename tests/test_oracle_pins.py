@@ -408,3 +408,59 @@ def test_sublayer_zero_output_projection_is_identity_and_unit_rms_update():
     upd = y - x
     np.testing.assert_allclose(np.sqrt(np.mean(upd * upd, -1)), 1.0, rtol=1e-6)
     del g
+
+
+def test_decode_sublayer_at_slot0_equals_one_token_sublayer():
+    """With step = 0 the memory holds only the new token: the decode sub-layer
+    must reduce to the cache-free sub-layer on a one-token prompt, whatever
+    the cache holds beyond slot 0."""
+    B, d, Hq, Hkv, D, Tmax = 3, 32, 4, 2, 8, 6
+    p = gi.make_sublayer_inputs(B, 1, d, Hq, Hkv, D, seed=11, distinct_scales=True)
+    x = orc.bf16_bits_to_f64(p["x"])
+    w = (p["wq"], p["sq"], p["wk"], p["sk"], p["wv"], p["sv"], p["wo"], p["so"])
+    g = np.random.default_rng(41)
+    kc = g.standard_normal((B, Tmax, Hkv, D)) * 3
+    vc = g.standard_normal((B, Tmax, Hkv, D)) * 3
+    step = np.zeros(B, np.int32)
+    y, kc2, vc2, ns = orc.decode_sublayer(x, kc, vc, step, *w, Hq, Hkv, D, 0.3, io=None)
+    ref = orc.sublayer(x, *w, Hq, Hkv, D, 0.3, io=None)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(ns, 1)
+    np.testing.assert_array_equal(kc2[:, 1:], kc[:, 1:])
+    np.testing.assert_array_equal(vc2[:, 1:], vc[:, 1:])
+
+
+def test_decode_sublayer_continues_a_prompt():
+    """Token T-1 decoded against a memory that holds the roped keys and the
+    values of tokens 0..T-2 reproduces row T-1 of the cache-free sub-layer over
+    the whole prompt (causality makes the earlier rows irrelevant to it)."""
+    B, T, d, Hq, Hkv, D, Tmax = 2, 7, 32, 6, 2, 8, 12
+    p = gi.make_sublayer_inputs(B, T, d, Hq, Hkv, D, seed=12, distinct_scales=True)
+    x = orc.bf16_bits_to_f64(p["x"])
+    w = (p["wq"], p["sq"], p["wk"], p["sk"], p["wv"], p["sv"], p["wo"], p["so"])
+    full = orc.sublayer(x, *w, Hq, Hkv, D, 0.4, io=None)
+    # memory contents for tokens 0..T-2, from the definitions of the K/V path
+    n = orc.rmsnorm(x[:, : T - 1], None, 1e-5)
+    k = orc.linear_int8(n, p["wk"], p["sk"]).reshape(B, T - 1, Hkv, D)
+    v = orc.linear_int8(n, p["wv"], p["sv"]).reshape(B, T - 1, Hkv, D)
+    g = np.random.default_rng(42)
+    kc = g.standard_normal((B, Tmax, Hkv, D)) * 4
+    vc = g.standard_normal((B, Tmax, Hkv, D)) * 4
+    kc[:, : T - 1] = orc.rope(k, np.broadcast_to(np.arange(T - 1), (B, T - 1)))
+    vc[:, : T - 1] = v
+    step = np.full(B, T - 1, np.int32)
+    y, _, _, ns = orc.decode_sublayer(x[:, T - 1:], kc, vc, step, *w, Hq, Hkv, D, 0.4, io=None)
+    np.testing.assert_array_equal(ns, T)
+    np.testing.assert_allclose(y[:, 0], full[:, T - 1], rtol=1e-11, atol=1e-11)
+
+
+def test_decode_sublayer_zero_output_projection_is_identity():
+    B, d, Hq, Hkv, D, Tmax = 2, 16, 2, 1, 8, 4
+    p = gi.make_sublayer_inputs(B, 1, d, Hq, Hkv, D, seed=13)
+    x = orc.bf16_bits_to_f64(p["x"])
+    kc = np.zeros((B, Tmax, Hkv, D))
+    vc = np.zeros((B, Tmax, Hkv, D))
+    y, _, _, _ = orc.decode_sublayer(x, kc, vc, np.array([1, 3], np.int32), p["wq"], p["sq"],
+                                     p["wk"], p["sk"], p["wv"], p["sv"], np.zeros_like(p["wo"]),
+                                     p["so"], Hq, Hkv, D, 0.35)
+    np.testing.assert_array_equal(y, x)
