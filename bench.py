@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--only", default="", help="comma list of prefill,decode_b1,decode_ragged,sublayer (default: all)")
+    ap.add_argument("--only", default="", help="comma list of prefill,decode_b1,decode_ragged,sublayer,"
+                    "decode_sublayer_b1,decode_sublayer_b32 (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (HBM counter calibration)")
@@ -162,6 +163,50 @@ def bench_sublayer(torch, grok, pipe, U, gi, steps, warmup):
             "unit": "TFLOP/s", "flop_per_step": flop}
 
 
+def bench_decode_sublayer(torch, grok, pipe, U, gi, name, steps, warmup, replicas):
+    """One step = the attention sub-layer for one new token per sequence: pre-norm,
+    Q|K|V projection (one launch), RoPE + append, decode attention, output
+    projection, post-norm + residual. `replicas` copies of the weights and caches
+    are cycled so that each step streams them from HBM, not from the last-level
+    cache."""
+    w = gi.WORKLOADS[name]
+    p = gi.make_workload(name)
+    x, stp = U.dev_bf16(p["x"]), U.dev(p["step"])
+    wnames = ("wq", "sq", "wk", "sk", "wv", "sv", "wo", "so")
+    steps_obj = []
+    for _ in range(replicas):
+        kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+        ww = [U.dev(p[k]) for k in wnames]
+        steps_obj.append(pipe.DecodeSublayerStep(x, kc, vc, stp, *ww, w.Hq, w.Hkv, w.D, w.attn_mult,
+                                                 w.softcap, w.eps))
+    B, d, D, Hq, Hkv = w.B, w.d_model, w.D, w.Hq, w.Hkv
+    L = p["kv_len"].astype(np.int64)
+    del p
+    cols = Hq * D + 2 * Hkv * D
+    w_bytes = d * cols + Hq * D * d + 4 * (cols + d)       # int8 weights + fp32 scales
+    kv_bytes = int(L.sum()) * Hkv * D * 2 * 2               # valid K and V slots, once
+    io_bytes = B * (2 * d * 2 + 2 * Hkv * D * 2)            # x in, y out, new k/v written
+    nbytes = w_bytes + kv_bytes + io_bytes
+    graphs = [pipe.capture(s_) for s_ in steps_obj]
+    sec = time_replays(torch, graphs, steps, warmup)
+
+    def proj(i):  # both few-row projections of one step
+        s_ = steps_obj[i % len(steps_obj)]
+        wq, sq, wk, sk, wv, sv, wo, so = s_.w
+        grok.grok_linear_int8_gemv(s_.n, [wq, wk, wv], [sq, sk, sv], [s_.q, s_.k, s_.v], s_.qkv_ws)
+        grok.grok_linear_int8_gemv(s_.attn, [wo], [so], [s_.o], s_.o_ws)
+
+    proj_ms = time_kernel(torch, proj, max(steps, 2 * len(steps_obj)))
+    pbytes = d * cols + Hq * D * d + 4 * (cols + d) + B * 2 * (d + cols + Hq * D + d)
+    return {
+        "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",
+        "bytes_per_step": nbytes, "kernel": "gemv_int8_kernel (Q|K|V and O projections)",
+        "kernel_ms": proj_ms, "kernel_gbs": pbytes / (proj_ms * 1e-3) / 1e9,
+        "kernel_frac_of_hbm_peak": pbytes / (proj_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "replicas": replicas,
+    }
+
+
 def cpu_baseline(gi, orc):
     """The fp64 oracle on a bounded sample of the 8k prefill: all 48 heads of
     256 query rows spread over the sequence (RoPE of the sampled q rows and of
@@ -207,7 +252,8 @@ def main():
     import gqa_inputs as gi
     import gpu_util as U
 
-    only = set(args.only.split(",")) if args.only else {"prefill", "decode_b1", "decode_ragged", "sublayer"}
+    only = set(args.only.split(",")) if args.only else {"prefill", "decode_b1", "decode_ragged", "sublayer",
+                                                        "decode_sublayer_b1", "decode_sublayer_b32"}
     res = {}
     if args.copy_calibration:
         # a plain copy of known size: reads and writes exactly 256 MiB
@@ -234,6 +280,14 @@ def main():
     if "sublayer" in only:
         res["sublayer"] = bench_sublayer(torch, grok, pipe, U, gi, max(1, args.steps // 4), min(args.warmup, 2))
         print(f"# sublayer done: {res['sublayer']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    for key, name, reps in (("decode_sublayer_b1", "decode_sublayer_b1_t8192", 4),
+                            ("decode_sublayer_b32", "decode_sublayer_b32_t8192", 2)):
+        if key in only:
+            res[key] = bench_decode_sublayer(torch, grok, pipe, U, gi, name, args.steps, args.warmup, reps)
+            print(f"# {key} done: {res[key]['value']:.1f} GB/s, {res[key]['ms_per_step'] * 1e3:.1f} us/step",
+                  file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     head = res.get("prefill") or next(iter(res.values()))
     line = {

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "GrokError", "LIB_PATH", "lib", "GROK_BF16", "GROK_F32",
     "grok_abi_version", "grok_status_string", "grok_last_error",
-    "grok_rmsnorm", "grok_linear_int8", "grok_rope", "grok_kv_append",
+    "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_gemv",
+    "grok_linear_int8_gemv_workspace_bytes", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_workspace_bytes",
 ]
 
@@ -30,7 +31,7 @@ GROK_OK, GROK_EHIP, GROK_ENOMEM, GROK_EINVAL, GROK_ERANGE = 0, -5, -12, -22, -34
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m gqa_attention_grok_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python gqa_attention_grok_amd/build.py` "
         "(there is no non-HIP fallback)")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -42,6 +43,8 @@ _PROTOS = {
     "grok_last_error": (ctypes.c_char_p, []),
     "grok_rmsnorm": (_i, [_p, _p, _p, _p, _i64, _i, _f, _i, _p]),
     "grok_linear_int8": (_i, [_p, _p, _p, _p, _i64, _i, _i, _p]),
+    "grok_linear_int8_gemv": (_i, [_p, _i, _p, _p, _p, _p, _i64, _i, _p, _sz, _p]),
+    "grok_linear_int8_gemv_workspace_bytes": (_sz, [_i64, _i, _i, _p]),
     "grok_rope": (_i, [_p, _i, _i, _i, _i, _p, _f, _i, _p]),
     "grok_kv_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
@@ -129,6 +132,43 @@ def grok_linear_int8(x, w, scales, y):
     _check(lib.grok_linear_int8(_ptr(x), _ptr(w), _ptr(scales), _ptr(y), x.numel() // K, K, N,
                                 _stream(x)), "grok_linear_int8")
     return y
+
+
+def _gemv_arrays(ws, ss, ys, ns):
+    n = len(ns)
+    return ((_p * n)(*ws), (_p * n)(*ss), (_p * n)(*ys), (_i * n)(*ns))
+
+
+def grok_linear_int8_gemv_workspace_bytes(M, K, Ns) -> int:
+    """Workspace bytes of grok_linear_int8_gemv for x [M, K] and outputs of Ns channels."""
+    n = len(Ns)
+    return lib.grok_linear_int8_gemv_workspace_bytes(M, K, n, ctypes.cast((_i * n)(*Ns), _p))
+
+
+def grok_linear_int8_gemv(x, ws, scales, ys, workspace):
+    """ys[p] [M, N_p] = x [M, K] @ (ws[p] [K, N_p] int8 * scales[p] [N_p]) for up to
+    three matrices sharing x, in one launch. ``workspace``: zero-filled once before
+    its first use (uint8 tensor of grok_linear_int8_gemv_workspace_bytes bytes)."""
+    _need(x, "x", torch.bfloat16)
+    _need(workspace, "workspace")
+    if not (len(ws) == len(scales) == len(ys)):
+        raise ValueError("ws, scales and ys must have the same length")
+    K = ws[0].shape[0]
+    for p, (w, s, y) in enumerate(zip(ws, scales, ys)):
+        _need(w, f"ws[{p}]", torch.int8, 2)
+        _need(s, f"scales[{p}]", torch.float32, 1)
+        _need(y, f"ys[{p}]", torch.bfloat16)
+        if w.shape[0] != K:
+            raise ValueError("all weights must have the same K")
+    Ns = [w.shape[1] for w in ws]
+    wa, sa, ya, na = _gemv_arrays([_ptr(w) for w in ws], [_ptr(s) for s in scales],
+                                  [_ptr(y) for y in ys], Ns)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.grok_linear_int8_gemv(_ptr(x), len(ws), ctypes.cast(wa, _p), ctypes.cast(sa, _p),
+                                     ctypes.cast(ya, _p), ctypes.cast(na, _p), x.numel() // K, K,
+                                     _ptr(workspace), ws_bytes, _stream(x)),
+           "grok_linear_int8_gemv")
+    return ys
 
 
 def grok_rope(x, offset=None, base=10000.0):

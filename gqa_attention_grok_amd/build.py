@@ -1,6 +1,6 @@
 """Compile the HIP library ``libgrokattn.so`` for gfx950, in-tree.
 
-``python -m gqa_attention_grok_amd.build`` (or ``build()``) runs hipcc once
+``python gqa_attention_grok_amd/build.py`` (or ``build()``) runs hipcc once
 over every ``csrc/*.hip`` file and links them into one shared library next to
 this file. hipcc cross-compiles for gfx950 without a GPU present.
 """

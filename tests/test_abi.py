@@ -24,14 +24,18 @@ def declared_symbols():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from gqa_attention_grok_amd.build import build
-        build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_grok_build", os.path.join(os.path.dirname(HEADER), "..", "gqa_attention_grok_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return ctypes.CDLL(LIB)
 
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 12, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -151,3 +155,52 @@ def test_decode_validation_and_workspace(lib):
     assert call(Hq=44) == EINVAL
     assert call(Hq=136, Hkv=8) == EINVAL  # 17 heads per KV head
     assert call(cap=-1.0) == EINVAL
+
+
+def test_gemv_validation_and_workspace(lib):
+    wsb = lib.grok_linear_int8_gemv_workspace_bytes
+    wsb.restype = ctypes.c_size_t
+    wsb.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+
+    def Ns(*v):
+        return ctypes.cast((ctypes.c_int * len(v))(*v), ctypes.c_void_p)
+
+    # up to 4 rows: whole K per workgroup, nothing but the (unused) ticket line
+    assert wsb(1, 6144, 3, Ns(6144, 1024, 1024)) == 256
+    assert wsb(4, 6144, 1, Ns(6144)) == 256
+    # 5 rows: one row tile; Q|K|V = 48 + 8 + 8 blocks of 128 channels, K cut
+    # into 16 slices of 384 rows: tickets (one 256-byte line) + [64][16][5][128] fp32
+    assert wsb(5, 6144, 3, Ns(6144, 1024, 1024)) == 256 + 64 * 16 * 5 * 128 * 4
+    # output projection: 48 blocks, 16 slices
+    assert wsb(8, 6144, 1, Ns(6144)) == 256 + 48 * 16 * 8 * 128 * 4
+    # 32 rows: two row tiles, fewer slices (8) of 768 rows
+    assert wsb(32, 6144, 3, Ns(6144, 1024, 1024)) == 256 + 64 * 8 * 32 * 128 * 4
+    # more rows than one launch takes: sized for 32
+    assert wsb(100, 6144, 3, Ns(6144, 1024, 1024)) == wsb(32, 6144, 3, Ns(6144, 1024, 1024))
+    # short K: one slice, tickets only
+    assert wsb(1, 64, 1, Ns(256)) == 256
+    assert wsb(1, 6144, 0, Ns(6144)) == 0
+    assert wsb(1, 6144, 4, Ns(8, 8, 8, 8)) == 0
+    assert wsb(1, 6140, 1, Ns(6144)) == 0
+    assert wsb(1, 6144, 1, Ns(6140)) == 0
+
+    n = wsb(8, 6144, 1, Ns(6144))
+    arr = (ctypes.c_void_p * 3)(0x10000, 0x10000, 0x10000)
+    parr = ctypes.cast(arr, ctypes.c_void_p)
+    f = lib.grok_linear_int8_gemv
+    f.restype = ctypes.c_int
+
+    def call(x=FAKE, n_mats=1, N=None, M=8, K=6144, ws=FAKE, nbytes=n, w=parr):
+        return f(x, i(n_mats), w, parr, parr, N if N is not None else Ns(6144, 6144, 6144), i64(M), i(K),
+                 ws, ctypes.c_size_t(nbytes), None)
+    assert call(nbytes=n - 1) == ENOMEM
+    assert call(n_mats=0) == EINVAL
+    assert call(K=6143) == EINVAL
+    assert call(N=Ns(6148)) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(ws=ctypes.c_void_p(0x10008)) == EINVAL  # workspace 16-byte alignment
+    bad = (ctypes.c_void_p * 3)(0x10004, 0x10000, 0x10000)
+    assert call(w=ctypes.cast(bad, ctypes.c_void_p)) == EINVAL  # weights 8-byte alignment
+    nul = (ctypes.c_void_p * 3)(0x10000, None, 0x10000)
+    assert call(n_mats=2, N=Ns(6144, 1024), nbytes=1 << 20, w=ctypes.cast(nul, ctypes.c_void_p)) == EINVAL
+    assert call(M=0, x=None, ws=None) == 0

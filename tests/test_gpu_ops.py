@@ -107,6 +107,69 @@ def test_linear_int8_scale_axis_and_empty(G):
     grok.grok_linear_int8(e, U.dev(w), U.dev(s), torch.empty((0, N), dtype=torch.bfloat16, device="cuda"))
 
 
+@pytest.mark.parametrize("M,K,Ns", [
+    (1, 6144, (6144, 1024, 1024)),  # one token's Q|K|V (few-row kernel, 256 blocks by XCD)
+    (4, 6144, (6144,)),             # four rows, 192 blocks
+    (2, 1000, (136, 8, 1024)),      # ragged K and channel blocks, 38 blocks (plain order)
+    (3, 8, (8,)),                   # the smallest shape
+    (5, 6144, (6144, 1024, 1024)),  # matrix cores: 64 blocks grouped by XCD, 16 slices
+    (32, 6144, (6144,)),            # two row tiles; the last slice runs past K
+    (5, 1000, (136, 8, 1024)),      # ragged K, partial channel blocks, 11 blocks
+    (17, 200, (264,)),              # two row tiles, two slices, partial block
+    (70, 512, (128, 256)),          # more than 32 rows: 32 + 32 + 6 on one workspace
+    (34, 512, (128, 256)),          # 32 rows on the matrix cores, then 2 on the few-row kernel
+    (16, 96, (1024,)),              # a single slice: no partial sums
+])
+def test_linear_int8_gemv(G, M, K, Ns):
+    grok, U, torch = G
+    g = gi.rng(7 * M + K + sum(Ns))
+    xb = gi.normal_bf16(g, (M, K))
+    ws = [gi.int8_uniform(g, (K, n)) for n in Ns]
+    ss = [(0.02 / 127 * g.uniform(0.5, 1.5, n)).astype(np.float32) for n in Ns]
+    x, dw, ds = U.dev_bf16(xb), [U.dev(w) for w in ws], [U.dev(s) for s in ss]
+    ys = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in Ns]
+    nb = grok.grok_linear_int8_gemv_workspace_bytes(M, K, list(Ns))
+    work = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    print(f"gemv M={M} K={K} Ns={Ns} workspace {nb} B", flush=True)
+    grok.grok_linear_int8_gemv(x, dw, ds, ys, work)
+    x64 = orc.bf16_bits_to_f64(xb)
+    first = [U.bits(y).copy() for y in ys]
+    for p in range(len(Ns)):
+        U.assert_bf16_close(U.host(ys[p]), orc.linear_int8(x64, ws[p], ss[p]), f"gemv matrix {p}")
+    # every ticket is back at zero, and a second call on the same workspace
+    # gives the same bits (the slices are added in a fixed order)
+    ncb = sum((n + 127) // 128 for n in Ns)
+    assert int(work[: 4 * ncb].sum().item()) == 0
+    for y in ys:
+        y.fill_(0)
+    grok.grok_linear_int8_gemv(x, dw, ds, ys, work)
+    for p in range(len(Ns)):
+        np.testing.assert_array_equal(U.bits(ys[p]), first[p])
+
+
+def test_linear_int8_gemv_matches_tiled_kernel_and_empty(G):
+    """The few-row product and the tiled product compute the same sums in a
+    different order: equal to within an fp32 rounding of the bf16 result."""
+    grok, U, torch = G
+    M, K, N = 8, 6144, 1024
+    g = gi.rng(77)
+    xb = gi.normal_bf16(g, (M, K))
+    w = U.dev(gi.int8_uniform(g, (K, N)))
+    s = U.dev(np.full(N, 0.02 / 127, np.float32))
+    x = U.dev_bf16(xb)
+    a = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    work = torch.zeros(grok.grok_linear_int8_gemv_workspace_bytes(M, K, [N]), dtype=torch.uint8,
+                       device="cuda")
+    grok.grok_linear_int8_gemv(x, [w], [s], [a], work)
+    grok.grok_linear_int8(x, w, s, b)
+    d = np.abs(U.host(a) - U.host(b))
+    ulp = np.abs(U.host(b)) * 2.0 ** -7 + 1e-30
+    assert np.all(d <= ulp), float((d / ulp).max())
+    e = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    grok.grok_linear_int8_gemv(e, [w], [s], [torch.empty((0, N), dtype=torch.bfloat16, device="cuda")], work)
+
+
 # --------------------------------------------------------------------------
 # RoPE
 # --------------------------------------------------------------------------
@@ -341,3 +404,38 @@ def test_decode_bad_lengths_give_zero_rows_and_status(G):
     ref = orc.attention(orc.bf16_bits_to_f64(p["q"][1:2]), orc.bf16_bits_to_f64(p["k_cache"][1:2]),
                         orc.bf16_bits_to_f64(p["v_cache"][1:2]), mask, 1 / math.sqrt(D))
     U.assert_bf16_close(got[1:2], ref, "valid row next to bad ones")
+
+
+# --------------------------------------------------------------------------
+# Decode-time sub-layer (norm, few-row projections, RoPE + append, decode
+# attention, output projection, post-norm + residual)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,d,Hq,Hkv,lens,Tmax", [
+    (3, 256, 4, 2, [300, 77, 1], 300),   # full, short and single-slot memories
+    (2, 1024, 16, 2, [129, 1000], 1024),  # 8 query heads per KV head
+])
+def test_decode_sublayer(G, B, d, Hq, Hkv, lens, Tmax):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    D, mult = 128, 1 / math.sqrt(128)
+    p = gi.make_decode_sublayer_inputs(B, d, Hq, Hkv, D, Tmax, seed=B * d + Tmax, lengths=lens,
+                                       distinct_scales=True)
+    dv = {k: (U.dev_bf16(v) if v.dtype == np.uint16 else U.dev(v)) for k, v in p.items()}
+    st = pipe.DecodeSublayerStep(dv["x"], dv["k_cache"], dv["v_cache"], dv["step"], dv["wq"], dv["sq"],
+                                 dv["wk"], dv["sk"], dv["wv"], dv["sv"], dv["wo"], dv["so"], Hq, Hkv, D,
+                                 mult)
+    y = U.host(st())
+    torch.cuda.synchronize()
+    assert st.status.item() == 0
+    np.testing.assert_array_equal(st.kv_len.cpu().numpy(), lens)
+    x = orc.bf16_bits_to_f64(p["x"])
+    kc, vc = orc.bf16_bits_to_f64(p["k_cache"]), orc.bf16_bits_to_f64(p["v_cache"])
+    ref, kc2, vc2, _ = orc.decode_sublayer(x, kc, vc, p["step"], p["wq"], p["sq"], p["wk"], p["sk"],
+                                           p["wv"], p["sv"], p["wo"], p["so"], Hq, Hkv, D, mult)
+    # the appended slots (bf16 in both), then the output of the whole chain
+    for b in range(B):
+        s = lens[b] - 1
+        U.assert_bf16_close(U.host(st.k_cache[b, s]), kc2[b, s], f"appended k b={b}")
+        U.assert_bf16_close(U.host(st.v_cache[b, s]), vc2[b, s], f"appended v b={b}")
+    nt = ref - x
+    U.assert_bf16_close(y, ref, "decode sub-layer", magnitude=np.maximum(np.abs(ref), np.abs(nt)))

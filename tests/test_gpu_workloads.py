@@ -1,7 +1,8 @@
-"""The five named workloads at full size, run through the same step objects the
+"""The named workloads at full size, run through the same step objects the
 benchmark times, checked against the fp64 oracle: in full where the oracle is
-cheap (tiny prefill, both decodes), on sampled output rows that the oracle
-computes one by one otherwise (8k prefill, full sub-layer)."""
+cheap (tiny prefill, both decodes, the one-sequence decode sub-layer), on
+sampled output rows or sequences that the oracle computes one by one otherwise
+(8k prefill, full sub-layer, ragged decode sub-layer)."""
 import math
 
 import numpy as np
@@ -166,3 +167,36 @@ def test_sublayer_b4_t2048_sampled(G):
             errs.append(U.assert_bf16_close(U.host(y[b, t]), yt, f"sublayer output b={b} t={t}",
                                             magnitude=np.maximum(np.abs(yt), np.abs(nt))))
     print(f"sublayer sampled rows, max abs err {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("name,seqs", [
+    ("decode_sublayer_b1_t8192", None),
+    ("decode_sublayer_b32_t8192", (0, 13, 31)),
+])
+def test_decode_sublayer_workloads(G, name, seqs):
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS[name]
+    p = gi.make_workload(name)
+    dv = {k: (U.dev_bf16(v) if v.dtype == np.uint16 else U.dev(v)) for k, v in p.items()}
+    st = pipe.DecodeSublayerStep(dv["x"], dv["k_cache"], dv["v_cache"], dv["step"], dv["wq"], dv["sq"],
+                                 dv["wk"], dv["sk"], dv["wv"], dv["sv"], dv["wo"], dv["so"], w.Hq, w.Hkv,
+                                 w.D, w.attn_mult, w.softcap, w.eps)
+    y = U.host(st())
+    torch.cuda.synchronize()
+    assert st.status.item() == 0
+    np.testing.assert_array_equal(st.kv_len.cpu().numpy(), p["kv_len"])
+    del dv
+    seqs = range(w.B) if seqs is None else seqs
+    errs = []
+    for b in seqs:  # sequences are independent: the oracle takes them one at a time
+        sl = slice(b, b + 1)
+        x = orc.bf16_bits_to_f64(p["x"][sl])
+        ref, _, _, _ = orc.decode_sublayer(
+            x, orc.bf16_bits_to_f64(p["k_cache"][sl]), orc.bf16_bits_to_f64(p["v_cache"][sl]),
+            p["step"][sl], p["wq"], p["sq"], p["wk"], p["sk"], p["wv"], p["sv"], p["wo"], p["so"],
+            w.Hq, w.Hkv, w.D, w.attn_mult, w.softcap, w.eps)
+        nt = ref - x
+        errs.append(U.assert_bf16_close(y[sl], ref, f"{name} b={b} (length {p['kv_len'][b]})",
+                                        magnitude=np.maximum(np.abs(ref), np.abs(nt))))
+        print(f"{name} b={b}: rel L2 {U.rel_l2(y[sl], ref):.2e}", flush=True)
+    print(f"{name}: max abs err {max(errs):.2e}")
