@@ -20,8 +20,8 @@ import torch
 __all__ = [
     "GrokError", "LIB_PATH", "lib", "GROK_BF16", "GROK_F32",
     "grok_abi_version", "grok_status_string", "grok_last_error",
-    "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_gemv",
-    "grok_linear_int8_gemv_workspace_bytes", "grok_rope", "grok_kv_append",
+    "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
+    "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_workspace_bytes",
 ]
 
@@ -43,8 +43,9 @@ _PROTOS = {
     "grok_last_error": (ctypes.c_char_p, []),
     "grok_rmsnorm": (_i, [_p, _p, _p, _p, _i64, _i, _f, _i, _p]),
     "grok_linear_int8": (_i, [_p, _p, _p, _p, _i64, _i, _i, _p]),
-    "grok_linear_int8_gemv": (_i, [_p, _i, _p, _p, _p, _p, _i64, _i, _p, _sz, _p]),
-    "grok_linear_int8_gemv_workspace_bytes": (_sz, [_i64, _i, _i, _p]),
+    "grok_linear_int8_packed_bytes": (_sz, [_i, _i]),
+    "grok_linear_int8_pack": (_i, [_p, _p, _i, _i, _p]),
+    "grok_linear_int8_gemv": (_i, [_p, _i, _p, _p, _p, _p, _i64, _i, _p]),
     "grok_rope": (_i, [_p, _i, _i, _i, _i, _p, _f, _i, _p]),
     "grok_kv_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
@@ -134,39 +135,49 @@ def grok_linear_int8(x, w, scales, y):
     return y
 
 
-def _gemv_arrays(ws, ss, ys, ns):
-    n = len(ns)
-    return ((_p * n)(*ws), (_p * n)(*ss), (_p * n)(*ys), (_i * n)(*ns))
+def grok_linear_int8_packed_bytes(K, N) -> int:
+    return lib.grok_linear_int8_packed_bytes(K, N)
 
 
-def grok_linear_int8_gemv_workspace_bytes(M, K, Ns) -> int:
-    """Workspace bytes of grok_linear_int8_gemv for x [M, K] and outputs of Ns channels."""
-    n = len(Ns)
-    return lib.grok_linear_int8_gemv_workspace_bytes(M, K, n, ctypes.cast((_i * n)(*Ns), _p))
+def grok_linear_int8_pack(w, w_packed=None):
+    """Packed form of the int8 weights w [K, N] for grok_linear_int8_gemv (a new
+    int8 tensor of grok_linear_int8_packed_bytes(K, N) bytes unless one is given)."""
+    _need(w, "w", torch.int8, 2)
+    K, N = w.shape
+    nbytes = grok_linear_int8_packed_bytes(K, N)
+    if w_packed is None:
+        w_packed = torch.empty(nbytes, dtype=torch.int8, device=w.device)
+    _need(w_packed, "w_packed", torch.int8)
+    if w_packed.numel() != nbytes:
+        raise ValueError(f"w_packed must hold {nbytes} bytes")
+    _check(lib.grok_linear_int8_pack(_ptr(w), _ptr(w_packed), K, N, _stream(w)), "grok_linear_int8_pack")
+    return w_packed
 
 
-def grok_linear_int8_gemv(x, ws, scales, ys, workspace):
-    """ys[p] [M, N_p] = x [M, K] @ (ws[p] [K, N_p] int8 * scales[p] [N_p]) for up to
-    three matrices sharing x, in one launch. ``workspace``: zero-filled once before
-    its first use (uint8 tensor of grok_linear_int8_gemv_workspace_bytes bytes)."""
+def grok_linear_int8_gemv(x, w_packed, scales, ys):
+    """ys[p] [M, N_p] = x [M, K] @ (W_p * scales[p]) for up to three matrices that
+    share x, in one launch; w_packed[p] is grok_linear_int8_pack(W_p)."""
     _need(x, "x", torch.bfloat16)
-    _need(workspace, "workspace")
-    if not (len(ws) == len(scales) == len(ys)):
-        raise ValueError("ws, scales and ys must have the same length")
-    K = ws[0].shape[0]
-    for p, (w, s, y) in enumerate(zip(ws, scales, ys)):
-        _need(w, f"ws[{p}]", torch.int8, 2)
+    if not (len(w_packed) == len(scales) == len(ys)):
+        raise ValueError("w_packed, scales and ys must have the same length")
+    K = x.shape[-1]
+    M = x.numel() // K
+    Ns = []
+    for p, (w, s, y) in enumerate(zip(w_packed, scales, ys)):
+        _need(w, f"w_packed[{p}]", torch.int8)
         _need(s, f"scales[{p}]", torch.float32, 1)
         _need(y, f"ys[{p}]", torch.bfloat16)
-        if w.shape[0] != K:
-            raise ValueError("all weights must have the same K")
-    Ns = [w.shape[1] for w in ws]
-    wa, sa, ya, na = _gemv_arrays([_ptr(w) for w in ws], [_ptr(s) for s in scales],
-                                  [_ptr(y) for y in ys], Ns)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.grok_linear_int8_gemv(_ptr(x), len(ws), ctypes.cast(wa, _p), ctypes.cast(sa, _p),
-                                     ctypes.cast(ya, _p), ctypes.cast(na, _p), x.numel() // K, K,
-                                     _ptr(workspace), ws_bytes, _stream(x)),
+        N = s.shape[0]
+        if y.numel() != M * N or w.numel() != grok_linear_int8_packed_bytes(K, N):
+            raise ValueError(f"matrix {p}: sizes do not match x [{M}, {K}] and {N} channels")
+        Ns.append(N)
+    n = len(Ns)
+    wa = (_p * n)(*[_ptr(w) for w in w_packed])
+    sa = (_p * n)(*[_ptr(s) for s in scales])
+    ya = (_p * n)(*[_ptr(y) for y in ys])
+    na = (_i * n)(*Ns)
+    _check(lib.grok_linear_int8_gemv(_ptr(x), n, ctypes.cast(wa, _p), ctypes.cast(sa, _p),
+                                     ctypes.cast(ya, _p), ctypes.cast(na, _p), M, K, _stream(x)),
            "grok_linear_int8_gemv")
     return ys
 

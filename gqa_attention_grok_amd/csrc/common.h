@@ -63,18 +63,12 @@ hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, 
                             const RopeFreqs &f, hipStream_t s);
 hipError_t launch_linear_int8(const void *x, const int8_t *w, const float *scales, void *y,
                               int64_t M, int K, int N, hipStream_t s);
-// Split of the few-row int8 Linear: `rows` (<= 32) rows per launch in `mt`
-// tiles of 16, `s` slices of K of `j` 32-row steps per wave, `ncb` column
-// blocks of 128 channels; `ws_bytes` of workspace (tickets + slice sums).
-struct GemvPlan {
-  int rows, mt, s, j, ncb;
-  size_t ws_bytes;
-};
-GemvPlan gemv_plan(int64_t M, int K, int ncb);
-int gemv_column_blocks(int n, const int *N);
+// Few-row int8 Linear on packed weights (layout in linear_int8_gemv.hip).
+size_t gemv_packed_bytes(int K, int N);
+hipError_t launch_linear_int8_pack(const int8_t *w, int8_t *wp, int K, int N, hipStream_t s);
 hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
                                    const float *const *scales, void *const *y, const int *N,
-                                   int64_t M, int K, void *ws, hipStream_t s);
+                                   int64_t M, int K, hipStream_t s);
 hipError_t launch_prefill_generic(const void *q, const void *k, const void *v, int64_t kv_rows,
                                   const uint8_t *key_valid, void *out, int B, int T, int Hq,
                                   int Hkv, int D, float mult, float cap, int dtype,

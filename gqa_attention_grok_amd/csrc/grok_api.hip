@@ -75,47 +75,47 @@ int grok_linear_int8(const void *x, const int8_t *w, const float *scales, void *
   return hip_status(grok::launch_linear_int8(x, w, scales, y, M, K, N, stream), "linear_int8");
 }
 
-namespace {
-
-int gemv_check_sizes(const char *who, int64_t M, int K, int n, const int *N) {
-  if (n < 1 || n > 3) return fail(GROK_EINVAL, "%s: n_mats=%d outside [1, 3]", who, n);
-  if (!N) return fail(GROK_EINVAL, "%s: null N", who);
-  if (M < 0 || K < 1) return fail(GROK_EINVAL, "%s: bad shape M=%lld K=%d", who, (long long)M, K);
-  if (K % 8) return fail(GROK_EINVAL, "%s: K=%d not a multiple of 8", who, K);
-  int64_t cols = 0;
-  for (int p = 0; p < n; ++p) {
-    if (N[p] < 1 || N[p] % 8) return fail(GROK_EINVAL, "%s: N[%d]=%d must be a positive multiple of 8", who, p, N[p]);
-    cols += N[p];
-  }
-  if (cols > (int64_t(1) << 24)) return fail(GROK_EINVAL, "%s: too many output channels", who);
-  return GROK_OK;
+size_t grok_linear_int8_packed_bytes(int K, int N) {
+  if (K < 1 || N < 1 || K % 8 || N % 8) return 0;
+  return grok::gemv_packed_bytes(K, N);
 }
 
-}  // namespace
-
-size_t grok_linear_int8_gemv_workspace_bytes(int64_t M, int K, int n_mats, const int *N) {
-  if (gemv_check_sizes("linear_int8_gemv", M, K, n_mats, N) != GROK_OK) return 0;
-  return grok::gemv_plan(M < 1 ? 1 : M, K, grok::gemv_column_blocks(n_mats, N)).ws_bytes;
+int grok_linear_int8_pack(const int8_t *w, int8_t *w_packed, int K, int N, hipStream_t stream) {
+  if (K < 1 || N < 1 || K % 8 || N % 8)
+    return fail(GROK_EINVAL, "linear_int8_pack: K=%d and N=%d must be positive multiples of 8", K, N);
+  if (!w || !w_packed) return fail(GROK_EINVAL, "linear_int8_pack: null pointer");
+  if (reinterpret_cast<uintptr_t>(w_packed) % 16) return fail(GROK_EINVAL, "linear_int8_pack: misaligned w_packed");
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
+  const size_t na = static_cast<size_t>(K) * N, nb = grok::gemv_packed_bytes(K, N);
+  if (a < b + nb && b < a + na) return fail(GROK_EINVAL, "linear_int8_pack: w and w_packed overlap");
+  return hip_status(grok::launch_linear_int8_pack(w, w_packed, K, N, stream), "linear_int8_pack");
 }
 
-int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w,
+int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w_packed,
                           const float *const *scales, void *const *y, const int *N, int64_t M,
-                          int K, void *workspace, size_t ws_bytes, hipStream_t stream) {
-  const int st = gemv_check_sizes("linear_int8_gemv", M, K, n_mats, N);
-  if (st != GROK_OK) return st;
-  if (M == 0) return ok();
-  if (!x || !w || !scales || !y || !workspace) return fail(GROK_EINVAL, "linear_int8_gemv: null pointer");
-  uintptr_t a16 = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(workspace), a8 = 0;
+                          int K, hipStream_t stream) {
+  if (n_mats < 1 || n_mats > 3) return fail(GROK_EINVAL, "linear_int8_gemv: n_mats=%d outside [1, 3]", n_mats);
+  if (!N) return fail(GROK_EINVAL, "linear_int8_gemv: null N");
+  if (M < 0 || K < 1 || K % 8)
+    return fail(GROK_EINVAL, "linear_int8_gemv: bad shape M=%lld K=%d (K a positive multiple of 8)", (long long)M, K);
+  int64_t blocks = 0;
   for (int p = 0; p < n_mats; ++p) {
-    if (!w[p] || !scales[p] || !y[p]) return fail(GROK_EINVAL, "linear_int8_gemv: null pointer in matrix %d", p);
-    a16 |= reinterpret_cast<uintptr_t>(scales[p]);
-    a8 |= reinterpret_cast<uintptr_t>(w[p]) | reinterpret_cast<uintptr_t>(y[p]);
+    if (N[p] < 1 || N[p] % 8)
+      return fail(GROK_EINVAL, "linear_int8_gemv: N[%d]=%d must be a positive multiple of 8", p, N[p]);
+    blocks += (N[p] + 31) / 32;
   }
-  if (a16 % 16 || a8 % 8) return fail(GROK_EINVAL, "linear_int8_gemv: misaligned pointer");
-  const size_t need = grok::gemv_plan(M, K, grok::gemv_column_blocks(n_mats, N)).ws_bytes;
-  if (ws_bytes < need)
-    return fail(GROK_ENOMEM, "linear_int8_gemv: workspace %zu bytes < %zu needed", ws_bytes, need);
-  return hip_status(grok::launch_linear_int8_gemv(x, n_mats, w, scales, y, N, M, K, workspace, stream),
+  if (blocks > 0x7fffffff) return fail(GROK_EINVAL, "linear_int8_gemv: too many output channels");
+  if (M == 0) return ok();
+  if (!x || !w_packed || !scales || !y) return fail(GROK_EINVAL, "linear_int8_gemv: null pointer");
+  uintptr_t a16 = reinterpret_cast<uintptr_t>(x), a4 = 0, a2 = 0;
+  for (int p = 0; p < n_mats; ++p) {
+    if (!w_packed[p] || !scales[p] || !y[p]) return fail(GROK_EINVAL, "linear_int8_gemv: null pointer in matrix %d", p);
+    a16 |= reinterpret_cast<uintptr_t>(w_packed[p]);
+    a4 |= reinterpret_cast<uintptr_t>(scales[p]);
+    a2 |= reinterpret_cast<uintptr_t>(y[p]);
+  }
+  if (a16 % 16 || a4 % 4 || a2 % 2) return fail(GROK_EINVAL, "linear_int8_gemv: misaligned pointer");
+  return hip_status(grok::launch_linear_int8_gemv(x, n_mats, w_packed, scales, y, N, M, K, stream),
                     "linear_int8_gemv");
 }
 

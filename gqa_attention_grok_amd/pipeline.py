@@ -22,8 +22,8 @@ from __future__ import annotations
 import torch
 
 from . import (grok_attn_decode, grok_attn_decode_workspace_bytes, grok_attn_prefill,
-               grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
-               grok_linear_int8_gemv_workspace_bytes, grok_rmsnorm, grok_rope)
+               grok_kv_append, grok_linear_int8, grok_linear_int8_gemv, grok_linear_int8_pack,
+               grok_rmsnorm, grok_rope)
 
 
 def capture(step) -> "torch.cuda.CUDAGraph":
@@ -125,12 +125,15 @@ class DecodeSublayerStep:
     n = norm(x); q, k, v = n . W (one launch for the three); RoPE q and k at
     step[b] and append k, v at slot step[b]; decode attention over slots
     [0, step[b]+1); y = x + norm(attn . Wo). x [B, 1, d]; the caches are
-    updated in place, the step counter is not advanced (kv_len = step + 1)."""
+    updated in place, the step counter is not advanced (kv_len = step + 1).
+    The int8 weights are repacked once, here, into the layout the few-row
+    product streams."""
 
     def __init__(self, x, k_cache, v_cache, step, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D,
                  attn_mult, softcap=30.0, eps=1e-5, rope_base=10000.0):
         self.x, self.k_cache, self.v_cache, self.step = x, k_cache, v_cache, step
-        self.w = (wq, sq, wk, sk, wv, sv, wo, so)
+        self.packed = tuple(grok_linear_int8_pack(w_) for w_ in (wq, wk, wv, wo))
+        self.scales = (sq, sk, sv, so)
         self.attn_mult, self.softcap, self.eps, self.rope_base = attn_mult, softcap, eps, rope_base
         B, _, d = x.shape
         Tmax = k_cache.shape[1]
@@ -145,23 +148,24 @@ class DecodeSublayerStep:
         self.y = torch.empty((B, 1, d), dtype=bf, device=dev)
         self.kv_len = torch.empty(B, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
-        # zero-filled once; each projection call leaves its tickets at zero
-        self.qkv_ws = torch.zeros(grok_linear_int8_gemv_workspace_bytes(B, d, [Hq * D, Hkv * D, Hkv * D]),
-                                  dtype=torch.uint8, device=dev)
-        self.o_ws = torch.zeros(grok_linear_int8_gemv_workspace_bytes(B, Hq * D, [d]),
-                                dtype=torch.uint8, device=dev)
         nbytes = grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D)
         self.attn_ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
+    def project_qkv(self):
+        pq, pk, pv, _ = self.packed
+        sq, sk, sv, _ = self.scales
+        grok_linear_int8_gemv(self.n, [pq, pk, pv], [sq, sk, sv], [self.q, self.k, self.v])
+
+    def project_out(self):
+        grok_linear_int8_gemv(self.attn, [self.packed[3]], [self.scales[3]], [self.o])
+
     def __call__(self):
-        wq, sq, wk, sk, wv, sv, wo, so = self.w
         grok_rmsnorm(self.x, self.n, eps=self.eps)
-        grok_linear_int8_gemv(self.n, [wq, wk, wv], [sq, sk, sv], [self.q, self.k, self.v],
-                              self.qkv_ws)
+        self.project_qkv()
         grok_kv_append(self.k_cache, self.v_cache, self.k, self.v, self.step, q_inout=self.q,
                        new_step=self.kv_len, status=self.status, rope_base=self.rope_base)
         grok_attn_decode(self.q, self.k_cache, self.v_cache, self.kv_len, self.attn, self.attn_ws,
                          self.attn_mult, self.softcap, status=self.status)
-        grok_linear_int8_gemv(self.attn, [wo], [so], [self.o], self.o_ws)
+        self.project_out()
         grok_rmsnorm(self.o, self.y, residual=self.x, eps=self.eps)
         return self.y

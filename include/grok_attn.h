@@ -87,40 +87,43 @@ GROK_API int grok_linear_int8(const void *x, const int8_t *w, const float *scale
                      int64_t M, int K, int N, hipStream_t stream);
 
 /*
+ * Packed form of an int8 weight matrix for grok_linear_int8_gemv (a pure
+ * permutation of its bytes, padded with zeros): 1024-byte tiles of 64 rows x
+ * 16 columns, KP = ceil(K/64) tiles per 16-column block, block j's tiles
+ * contiguous and in K order; byte 16*l + 8*h + e (l < 64, h < 2, e < 8) of
+ * tile (j, i), at offset (j*KP + i)*1024, holds
+ *   w[64*i + 32*h + 8*(l/16) + e][16*j + l%16]   (0 past K or N).
+ * grok_linear_int8_packed_bytes returns ceil(K/64) * ceil(N/16) * 1024, or 0
+ * on bad sizes. grok_linear_int8_pack writes that many bytes.
+ *   w         [K, N] int8 (device); w_packed device, 16-byte aligned, must not
+ *             overlap w.
+ * Errors: EINVAL for NULL pointers, K or N not a positive multiple of 8, a
+ * misaligned w_packed, or overlapping buffers.
+ */
+GROK_API size_t grok_linear_int8_packed_bytes(int K, int N);
+GROK_API int grok_linear_int8_pack(const int8_t *w, int8_t *w_packed, int K, int N,
+                                   hipStream_t stream);
+
+/*
  * int8-weight Linear for a few rows, as in decoding where every sequence
  * contributes one row ([ch4] §4.1, §4.1.1; the query, key and value
  * projections of one token, §4.5.1, share their input): for p < n_mats,
  *   y[p] = x @ (w[p] * scales[p])
  * with the numerics of grok_linear_int8 (exact int8, fp32 sums, channel scale
- * applied to the fp32 sum, bf16 result), the sums over K being taken in a
- * fixed order, so repeated calls give identical bits.
- *   x          [M, K] bf16 (device).
- *   w, scales, y, N   host arrays of n_mats (1..3) entries: w[p] [K, N[p]]
- *              int8, scales[p] [N[p]] fp32, y[p] [M, N[p]] bf16 (device
- *              pointers; y[p] must not overlap x or each other).
- *   workspace  device scratch of at least grok_linear_int8_gemv_workspace_bytes
- *              bytes, 16-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE. Its
- *              first bytes are one ticket per block of 128 output channels,
- *              which every call leaves at zero again, followed by per-slice
- *              partial sums: later calls with the same n_mats and N (any M
- *              and K) reuse it as is, while a call with other output sizes
- *              needs a workspace of its own (or one zero-filled again).
- *              Calls that overlap in time must not share a workspace.
- * The weights are streamed once per 32 rows of x (larger M is processed 32
- * rows at a time): for M in the hundreds or more, grok_linear_int8 is the
- * faster call.
- * Errors: EINVAL for NULL pointers, n_mats outside [1, 3], M < 0, K < 1,
- * N[p] < 1, K or N[p] not a multiple of 8, x, scales[p] or workspace not
- * 16-byte aligned, w[p] or y[p] not 8-byte aligned; ENOMEM if ws_bytes is too
- * small. M == 0 is a no-op.
+ * applied to the fp32 sum, bf16 result). The weights are read once per 32
+ * rows of x, in the packed form above, so the call runs at the speed of HBM
+ * for small M; for M in the hundreds or more, grok_linear_int8 is faster.
+ *   x          [M, K] bf16 (device), 16-byte aligned.
+ *   w_packed, scales, y, N   host arrays of n_mats (1..3) entries of device
+ *              pointers: w_packed[p] the packed form of a [K, N[p]] int8
+ *              matrix (16-byte aligned), scales[p] [N[p]] fp32, y[p]
+ *              [M, N[p]] bf16 (must not overlap x or each other).
+ * Errors: EINVAL for NULL pointers, n_mats outside [1, 3], M < 0, K or N[p]
+ * not a positive multiple of 8, or misaligned pointers. M == 0 is a no-op.
  */
-GROK_API int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w,
+GROK_API int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w_packed,
                                    const float *const *scales, void *const *y, const int *N,
-                                   int64_t M, int K, void *workspace, size_t ws_bytes,
-                                   hipStream_t stream);
-
-/* Workspace bytes grok_linear_int8_gemv needs for these sizes (0 on bad sizes). */
-GROK_API size_t grok_linear_int8_gemv_workspace_bytes(int64_t M, int K, int n_mats, const int *N);
+                                   int64_t M, int K, hipStream_t stream);
 
 /*
  * Rotary embedding, in place ([ch4] §4.3, §4.3.1): for x [B, T, H, D] and the

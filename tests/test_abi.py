@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 13, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -157,50 +157,43 @@ def test_decode_validation_and_workspace(lib):
     assert call(cap=-1.0) == EINVAL
 
 
-def test_gemv_validation_and_workspace(lib):
-    wsb = lib.grok_linear_int8_gemv_workspace_bytes
-    wsb.restype = ctypes.c_size_t
-    wsb.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+def test_pack_and_gemv_validation(lib):
+    pb = lib.grok_linear_int8_packed_bytes
+    pb.restype = ctypes.c_size_t
+    # ceil(K/64) tiles of 64 rows x ceil(N/16) blocks of 16 channels, 1 KB each
+    assert pb(i(6144), i(6144)) == 96 * 384 * 1024 == 6144 * 6144
+    assert pb(i(1000), i(136)) == 16 * 9 * 1024
+    assert pb(i(8), i(8)) == 1024
+    assert pb(i(12), i(8)) == 0 and pb(i(8), i(0)) == 0
+
+    def pack(w=FAKE, wp=ctypes.c_void_p(0x100000), K=64, N=16):
+        return _c(lib, "grok_linear_int8_pack", w, wp, i(K), i(N), None)
+    assert pack(K=60) == EINVAL
+    assert pack(w=None) == EINVAL
+    assert pack(wp=ctypes.c_void_p(0x100008)) == EINVAL      # 16-byte alignment
+    assert pack(wp=ctypes.c_void_p(0x10200)) == EINVAL       # overlaps w [0x10000, +1024)
+    assert "overlap" in _err(lib)
+
+    f = lib.grok_linear_int8_gemv
+    f.restype = ctypes.c_int
 
     def Ns(*v):
         return ctypes.cast((ctypes.c_int * len(v))(*v), ctypes.c_void_p)
 
-    # up to 4 rows: whole K per workgroup, nothing but the (unused) ticket line
-    assert wsb(1, 6144, 3, Ns(6144, 1024, 1024)) == 256
-    assert wsb(4, 6144, 1, Ns(6144)) == 256
-    # 5 rows: one row tile; Q|K|V = 48 + 8 + 8 blocks of 128 channels, K cut
-    # into 16 slices of 384 rows: tickets (one 256-byte line) + [64][16][5][128] fp32
-    assert wsb(5, 6144, 3, Ns(6144, 1024, 1024)) == 256 + 64 * 16 * 5 * 128 * 4
-    # output projection: 48 blocks, 16 slices
-    assert wsb(8, 6144, 1, Ns(6144)) == 256 + 48 * 16 * 8 * 128 * 4
-    # 32 rows: two row tiles, fewer slices (8) of 768 rows
-    assert wsb(32, 6144, 3, Ns(6144, 1024, 1024)) == 256 + 64 * 8 * 32 * 128 * 4
-    # more rows than one launch takes: sized for 32
-    assert wsb(100, 6144, 3, Ns(6144, 1024, 1024)) == wsb(32, 6144, 3, Ns(6144, 1024, 1024))
-    # short K: one slice, tickets only
-    assert wsb(1, 64, 1, Ns(256)) == 256
-    assert wsb(1, 6144, 0, Ns(6144)) == 0
-    assert wsb(1, 6144, 4, Ns(8, 8, 8, 8)) == 0
-    assert wsb(1, 6140, 1, Ns(6144)) == 0
-    assert wsb(1, 6144, 1, Ns(6140)) == 0
+    def arr(*v):
+        return ctypes.cast((ctypes.c_void_p * len(v))(*v), ctypes.c_void_p)
+    good = arr(0x10000, 0x10000, 0x10000)
 
-    n = wsb(8, 6144, 1, Ns(6144))
-    arr = (ctypes.c_void_p * 3)(0x10000, 0x10000, 0x10000)
-    parr = ctypes.cast(arr, ctypes.c_void_p)
-    f = lib.grok_linear_int8_gemv
-    f.restype = ctypes.c_int
-
-    def call(x=FAKE, n_mats=1, N=None, M=8, K=6144, ws=FAKE, nbytes=n, w=parr):
-        return f(x, i(n_mats), w, parr, parr, N if N is not None else Ns(6144, 6144, 6144), i64(M), i(K),
-                 ws, ctypes.c_size_t(nbytes), None)
-    assert call(nbytes=n - 1) == ENOMEM
+    def call(x=FAKE, n_mats=1, N=None, M=1, K=6144, w=good, y=good):
+        return f(x, i(n_mats), w, good, y, N if N is not None else Ns(6144, 6144, 6144), i64(M), i(K), None)
     assert call(n_mats=0) == EINVAL
+    assert call(n_mats=4) == EINVAL
     assert call(K=6143) == EINVAL
     assert call(N=Ns(6148)) == EINVAL
     assert call(x=None) == EINVAL
-    assert call(ws=ctypes.c_void_p(0x10008)) == EINVAL  # workspace 16-byte alignment
-    bad = (ctypes.c_void_p * 3)(0x10004, 0x10000, 0x10000)
-    assert call(w=ctypes.cast(bad, ctypes.c_void_p)) == EINVAL  # weights 8-byte alignment
-    nul = (ctypes.c_void_p * 3)(0x10000, None, 0x10000)
-    assert call(n_mats=2, N=Ns(6144, 1024), nbytes=1 << 20, w=ctypes.cast(nul, ctypes.c_void_p)) == EINVAL
-    assert call(M=0, x=None, ws=None) == 0
+    assert call(x=ctypes.c_void_p(0x10008)) == EINVAL          # x 16-byte alignment
+    assert call(w=arr(0x10008, 0x10000, 0x10000)) == EINVAL   # packed weights 16-byte alignment
+    assert call(y=arr(0x10001, 0x10000, 0x10000)) == EINVAL   # bf16 output alignment
+    assert call(n_mats=2, N=Ns(6144, 1024), w=arr(0x10000, None, 0x10000)) == EINVAL
+    assert call(M=-1) == EINVAL
+    assert call(M=0, x=None) == 0

@@ -107,18 +107,37 @@ def test_linear_int8_scale_axis_and_empty(G):
     grok.grok_linear_int8(e, U.dev(w), U.dev(s), torch.empty((0, N), dtype=torch.bfloat16, device="cuda"))
 
 
+def _packed_reference(w):
+    """The packed layout restated with NumPy index arithmetic: tile (j, i) at
+    (j * KP + i) * 1024, byte 16*l + 8*h + e = w[64i + 32h + 8(l//16) + e, 16j + l%16]."""
+    K, N = w.shape
+    KP, NP = -(-K // 64), -(-N // 16)
+    wpad = np.zeros((KP * 64, NP * 16), np.int8)
+    wpad[:K, :N] = w
+    # [j, i, l, h, e] -> w[64i + 32h + 8(l//16) + e, 16j + l%16]
+    j, i_, l, h, e = np.meshgrid(np.arange(NP), np.arange(KP), np.arange(64), np.arange(2), np.arange(8),
+                                 indexing="ij")
+    return wpad[64 * i_ + 32 * h + 8 * (l // 16) + e, 16 * j + l % 16].reshape(-1)
+
+
+@pytest.mark.parametrize("K,N", [(64, 16), (1000, 136), (8, 8), (6144, 1024)])
+def test_linear_int8_pack_layout(G, K, N):
+    grok, U, torch = G
+    w = gi.int8_uniform(gi.rng(K + N), (K, N))
+    wp = grok.grok_linear_int8_pack(U.dev(w))
+    np.testing.assert_array_equal(wp.cpu().numpy(), _packed_reference(w))
+
+
 @pytest.mark.parametrize("M,K,Ns", [
-    (1, 6144, (6144, 1024, 1024)),  # one token's Q|K|V (few-row kernel, 256 blocks by XCD)
-    (4, 6144, (6144,)),             # four rows, 192 blocks
-    (2, 1000, (136, 8, 1024)),      # ragged K and channel blocks, 38 blocks (plain order)
+    (1, 6144, (6144, 1024, 1024)),  # one token's Q|K|V: 256 workgroups of 32 channels
+    (4, 6144, (6144,)),             # four rows
+    (2, 1000, (136, 8, 1024)),      # ragged K and channel blocks
     (3, 8, (8,)),                   # the smallest shape
-    (5, 6144, (6144, 1024, 1024)),  # matrix cores: 64 blocks grouped by XCD, 16 slices
-    (32, 6144, (6144,)),            # two row tiles; the last slice runs past K
-    (5, 1000, (136, 8, 1024)),      # ragged K, partial channel blocks, 11 blocks
-    (17, 200, (264,)),              # two row tiles, two slices, partial block
-    (70, 512, (128, 256)),          # more than 32 rows: 32 + 32 + 6 on one workspace
-    (34, 512, (128, 256)),          # 32 rows on the matrix cores, then 2 on the few-row kernel
-    (16, 96, (1024,)),              # a single slice: no partial sums
+    (17, 6144, (6144, 1024, 1024)), # two row tiles
+    (32, 6144, (6144,)),
+    (17, 200, (264,)),
+    (70, 512, (128, 256)),          # more than 32 rows: 32 + 32 + 6
+    (34, 96, (1024, 24)),           # 32 + 2, a block with half its channels
 ])
 def test_linear_int8_gemv(G, M, K, Ns):
     grok, U, torch = G
@@ -126,23 +145,20 @@ def test_linear_int8_gemv(G, M, K, Ns):
     xb = gi.normal_bf16(g, (M, K))
     ws = [gi.int8_uniform(g, (K, n)) for n in Ns]
     ss = [(0.02 / 127 * g.uniform(0.5, 1.5, n)).astype(np.float32) for n in Ns]
-    x, dw, ds = U.dev_bf16(xb), [U.dev(w) for w in ws], [U.dev(s) for s in ss]
+    x = U.dev_bf16(xb)
+    wp = [grok.grok_linear_int8_pack(U.dev(w)) for w in ws]
+    ds = [U.dev(s) for s in ss]
     ys = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in Ns]
-    nb = grok.grok_linear_int8_gemv_workspace_bytes(M, K, list(Ns))
-    work = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-    print(f"gemv M={M} K={K} Ns={Ns} workspace {nb} B", flush=True)
-    grok.grok_linear_int8_gemv(x, dw, ds, ys, work)
+    print(f"gemv M={M} K={K} Ns={Ns}", flush=True)
+    grok.grok_linear_int8_gemv(x, wp, ds, ys)
     x64 = orc.bf16_bits_to_f64(xb)
     first = [U.bits(y).copy() for y in ys]
     for p in range(len(Ns)):
         U.assert_bf16_close(U.host(ys[p]), orc.linear_int8(x64, ws[p], ss[p]), f"gemv matrix {p}")
-    # every ticket is back at zero, and a second call on the same workspace
-    # gives the same bits (the slices are added in a fixed order)
-    ncb = sum((n + 127) // 128 for n in Ns)
-    assert int(work[: 4 * ncb].sum().item()) == 0
+    # a second call gives the same bits (the sums are taken in a fixed order)
     for y in ys:
         y.fill_(0)
-    grok.grok_linear_int8_gemv(x, dw, ds, ys, work)
+    grok.grok_linear_int8_gemv(x, wp, ds, ys)
     for p in range(len(Ns)):
         np.testing.assert_array_equal(U.bits(ys[p]), first[p])
 
@@ -159,15 +175,14 @@ def test_linear_int8_gemv_matches_tiled_kernel_and_empty(G):
     x = U.dev_bf16(xb)
     a = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
-    work = torch.zeros(grok.grok_linear_int8_gemv_workspace_bytes(M, K, [N]), dtype=torch.uint8,
-                       device="cuda")
-    grok.grok_linear_int8_gemv(x, [w], [s], [a], work)
+    wp = grok.grok_linear_int8_pack(w)
+    grok.grok_linear_int8_gemv(x, [wp], [s], [a])
     grok.grok_linear_int8(x, w, s, b)
     d = np.abs(U.host(a) - U.host(b))
     ulp = np.abs(U.host(b)) * 2.0 ** -7 + 1e-30
     assert np.all(d <= ulp), float((d / ulp).max())
     e = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
-    grok.grok_linear_int8_gemv(e, [w], [s], [torch.empty((0, N), dtype=torch.bfloat16, device="cuda")], work)
+    grok.grok_linear_int8_gemv(e, [wp], [s], [torch.empty((0, N), dtype=torch.bfloat16, device="cuda")])
 
 
 # --------------------------------------------------------------------------
