@@ -20,9 +20,11 @@
 //
 // Work split. A workgroup owns NB blocks of 16 channels and the whole K axis,
 // so no partial sums leave it; its 8 waves take contiguous ranges of tiles,
-// each with a ring of loads 6 to 8 steps deep. The A operand is 16 rows of x
-// (row m = lane % 16, zero beyond M). The 8 waves' sums meet in LDS, where
-// the channel scale is applied and bf16 written.
+// each with a ring of loads 6 to 16 steps deep. The A operand is 16 rows of x
+// (row m = lane % 16, zero beyond M), read from LDS for up to 4 rows (x is
+// copied there once per workgroup) and loaded with the weights otherwise.
+// The 8 waves' sums meet in LDS, where the channel scale is applied and bf16
+// written.
 //
 // Up to three matrices that share x (the query, key and value projections of
 // §4.5.1) are computed in one launch: their workgroups are numbered one after
@@ -78,13 +80,28 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// MT row tiles of 16 (M <= 16*MT), NB 16-channel blocks per workgroup, ring
-// of D steps (one step = one 64-row tile of each block plus its x).
-template <int MT, int NB, int D>
-__global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
-  constexpr int kLoads = NB + 2 * MT;  // load instructions per step
+// Pass registers filled by inline-assembly loads through empty asm statements
+// placed right after a wait: their uses cannot move above it (volatile asm
+// statements keep their order).
+template <int NW, int NX>
+__device__ __forceinline__ void tie_after_wait(u32x4 *w, u32x4 *x) {
+#pragma unroll
+  for (int v = 1; v < NW; ++v) asm volatile("" : "+v"(w[v]));
+#pragma unroll
+  for (int v = 0; v < NX; ++v) asm volatile("" : "+v"(x[v]));
+}
+
+// MT row tiles of 16 (M <= 16*MT), NB 16-channel blocks per workgroup, W
+// waves, a ring of D steps (one step = one 64-row tile of each block, plus
+// its x unless XL). With XL the M (<= 4) rows of x are first copied to LDS and
+// the A operands read from there.
+template <int MT, int NB, int W, int D, bool XL>
+__global__ __launch_bounds__(W * kWave) void gemv_packed_kernel(GemvArgs a) {
+  constexpr int kLoads = XL ? NB : NB + 2 * MT;  // ring loads per step
   static_assert((D - 1) * kLoads <= 63, "the wait count must fit vmcnt");
-  __shared__ float red[kWaves][kMaxRows][NB * kTileCols];
+  static_assert(!XL || MT == 1, "x in LDS is for at most 4 rows");
+  extern __shared__ f32x4 xs4[];  // XL: x rows [M][K] bf16
+  __shared__ float red[W][XL ? 4 : kMaxRows][NB * kTileCols];
   const int tid = threadIdx.x;
   const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
   const int M = a.M, K = a.K, KP = a.KP;
@@ -100,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
   const int NP = (N + kTileCols - 1) / kTileCols;
 
   // This wave's tiles: [i0, i1) of every block; blocks past NP re-read block j0.
-  const int i0 = static_cast<int>(static_cast<int64_t>(KP) * wv / kWaves);
-  const int i1 = static_cast<int>(static_cast<int64_t>(KP) * (wv + 1) / kWaves);
+  const int i0 = static_cast<int>(static_cast<int64_t>(KP) * wv / W);
+  const int i1 = static_cast<int>(static_cast<int64_t>(KP) * (wv + 1) / W);
   const int8_t *wb[NB];
 #pragma unroll
   for (int v = 0; v < NB; ++v)
@@ -117,42 +134,86 @@ __global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[v][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // With XL: x is copied to LDS with loads issued ahead of the ring's, so the
+  // wait below the ring's prologue covers them.
+  constexpr int kStage = XL ? 4 : 1;  // 16-byte x pieces per thread (M*K <= 4*W*64*8)
+  u32x4 st[kStage];
+  const int nst = XL ? M * K / 8 : 0;
+  if constexpr (XL) {
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int c = tid + r * W * kWave;
+      st[r] = load16(a.x + 8 * static_cast<int64_t>(c < nst ? c : 0));
+    }
+  }
+
   // Ring of D steps, loads as inline assembly with an explicit wait: when a
   // step is consumed, the (D-1) * kLoads loads of the later steps may still be
   // in flight (loads return in issue order). Steps past the wave's range
   // re-read its last tile (a cache hit) and are not consumed.
   u32x4 wr[D][NB];
-  u32x4 xa[D][MT][2];
+  u32x4 xa[XL ? 1 : D][MT][2];
   auto issue = [&](int slot, int i) {
     const int ic = i < i1 ? i : i1 - 1;
 #pragma unroll
     for (int v = 0; v < NB; ++v) wr[slot][v] = load16(wb[v] + static_cast<int64_t>(ic) * kTileBytes);
+    if constexpr (!XL) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+      for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = kTileRows * ic + 32 * h + 8 * g;
-        xa[slot][t][h] = load16(xr[t] + (k < K ? k : 0));
-      }
+        for (int h = 0; h < 2; ++h) {
+          const int k = kTileRows * ic + 32 * h + 8 * g;
+          xa[slot][t][h] = load16(xr[t] + (k < K ? k : 0));
+        }
+    }
   };
-  if (i1 > i0) {
+  const bool busy = i1 > i0;
+  if (busy) {
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(u, i0 + u);
+  }
+  if constexpr (XL) {
+    if (busy) {
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(D * kLoads) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) asm volatile("" : "+v"(st[r]));  // uses stay below the wait
+    bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int c = tid + r * W * kWave;
+      if (c < nst) *reinterpret_cast<u32x4 *>(xs + 8 * c) = st[r];
+    }
+    __syncthreads();
+  }
+  if (busy) {
     for (int c0 = i0; c0 < i1; c0 += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"((D - 1) * kLoads) : "memory");
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(wr[u][0]) : "n"((D - 1) * kLoads) : "memory");
+        tie_after_wait<NB, XL ? 0 : 2 * MT>(&wr[u][0], &xa[XL ? 0 : u][0][0]);
         __builtin_amdgcn_sched_barrier(0);
         const int i = c0 + u;
         if (i < i1) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const bool kok = kTileRows * i + 32 * h + 8 * g < K;
+            const int k = kTileRows * i + 32 * h + 8 * g;
+            const bool kok = k < K;
             bf16x8 A[MT];
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
               const bool ok = kok && 16 * t + i16 < M;
-              A[t] = __builtin_bit_cast(bf16x8, ok ? xa[u][t][h] : u32x4{0u, 0u, 0u, 0u});
+              u32x4 xv;
+              if constexpr (XL) {
+                const bf16_t *xs = reinterpret_cast<const bf16_t *>(xs4);
+                xv = *reinterpret_cast<const u32x4 *>(xs + static_cast<int64_t>(i16 < M ? i16 : 0) * K +
+                                                      (kok ? k : 0));
+              } else {
+                xv = xa[u][t][h];
+              }
+              A[t] = __builtin_bit_cast(bf16x8, ok ? xv : u32x4{0u, 0u, 0u, 0u});
             }
 #pragma unroll
             for (int v = 0; v < NB; ++v) {
@@ -181,13 +242,13 @@ __global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
         if (m < M) red[wv][m][kTileCols * v + i16] = acc[v][t][e];
       }
   __syncthreads();
-  for (int q = tid; q < M * NB * kTileCols; q += kThreads) {
+  for (int q = tid; q < M * NB * kTileCols; q += W * kWave) {
     const int m = q / (NB * kTileCols), c = q % (NB * kTileCols);
     const int n = kTileCols * j0 + c;
     if (n >= N) continue;
     float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < kWaves; ++u) sum += red[u][m][c];
+    for (int u = 0; u < W; ++u) sum += red[u][m][c];
     y[static_cast<int64_t>(m) * N + n] = f32_to_bf16(sum * sc[n]);
   }
 }
@@ -235,10 +296,22 @@ hipError_t launch_linear_int8_pack(const int8_t *w, int8_t *wp, int K, int N, hi
 hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
                                    const float *const *scales, void *const *y, const int *N,
                                    int64_t M, int K, hipStream_t stream) {
-  constexpr int NB = 2;
   for (int64_t r0 = 0; r0 < M; r0 += kMaxRows) {
-    GemvArgs a = {};
     const int rows = static_cast<int>(M - r0 < kMaxRows ? M - r0 : kMaxRows);
+    // Up to 4 rows: 16 channels per workgroup, x staged in LDS (when it fits
+    // the staging registers, 4 x 16 bytes per thread), 16 steps in flight;
+    // up to 16 rows: 32 channels, x from the ring; more: two row tiles.
+    int NB = 2;
+    bool xl = false;
+    GemvKernel k = gemv_packed_kernel<1, 2, kWaves, 8, false>;
+    if (rows > 16) {
+      k = gemv_packed_kernel<2, 2, kWaves, 6, false>;
+    } else if (rows <= 4 && static_cast<int64_t>(rows) * K <= 4 * kThreads * 8) {
+      xl = true;
+      NB = 1;
+      k = gemv_packed_kernel<1, 1, kWaves, 16, true>;
+    }
+    GemvArgs a = {};
     a.x = static_cast<const bf16_t *>(x) + r0 * K;
     int wg = 0;
     for (int q = 0; q < n; ++q) {
@@ -250,8 +323,8 @@ hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
     a.M = rows;
     a.K = K;
     a.KP = (K + kTileRows - 1) / kTileRows;
-    const GemvKernel k = rows <= 16 ? gemv_packed_kernel<1, NB, 8> : gemv_packed_kernel<2, NB, 6>;
-    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wg)), dim3(kThreads), 0, stream, a);
+    const size_t lds = xl ? static_cast<size_t>(rows) * K * 2 : 0;
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wg)), dim3(kThreads), lds, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
