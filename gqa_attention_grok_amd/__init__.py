@@ -21,7 +21,7 @@ __all__ = [
     "GrokError", "LIB_PATH", "lib", "GROK_BF16", "GROK_F32",
     "grok_abi_version", "grok_status_string", "grok_last_error",
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
-    "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_rope", "grok_kv_append",
+    "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_workspace_bytes",
 ]
 
@@ -46,6 +46,8 @@ _PROTOS = {
     "grok_linear_int8_packed_bytes": (_sz, [_i, _i]),
     "grok_linear_int8_pack": (_i, [_p, _p, _i, _i, _p]),
     "grok_linear_int8_gemv": (_i, [_p, _i, _p, _p, _p, _p, _i64, _i, _p]),
+    "grok_decode_qkv": (_i, [_p, _p, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                             _i, _i, _i, _i, _i, _i, _f, _p]),
     "grok_rope": (_i, [_p, _i, _i, _i, _i, _p, _f, _i, _p]),
     "grok_kv_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
@@ -180,6 +182,38 @@ def grok_linear_int8_gemv(x, w_packed, scales, ys):
                                      ctypes.cast(ya, _p), ctypes.cast(na, _p), M, K, _stream(x)),
            "grok_linear_int8_gemv")
     return ys
+
+
+def grok_decode_qkv(x, wq_packed, sq, wk_packed, sk, wv_packed, sv, q_out, k_cache, v_cache,
+                    step, new_step=None, status=None, prenorm=False, gamma=None, eps=1e-5,
+                    rope_base=10000.0):
+    """One new token per sequence: [n = rmsnorm(x)]; q_out = rope(n Wq) at step[b];
+    k_cache/v_cache slot step[b] = rope(n Wk), n Wv; new_step = step + 1."""
+    _need(x, "x", torch.bfloat16)
+    _need(q_out, "q_out", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    for t, n in ((wq_packed, "wq_packed"), (wk_packed, "wk_packed"), (wv_packed, "wv_packed")):
+        _need(t, n, torch.int8)
+    for t, n in ((sq, "sq"), (sk, "sk"), (sv, "sv")):
+        _need(t, n, torch.float32, 1)
+    _need(step, "step", torch.int32, 1)
+    _need(new_step, "new_step", torch.int32, 1)
+    _need(status, "status", torch.int32)
+    _need(gamma, "gamma", torch.float32, 1)
+    B, Tmax, Hkv, D = k_cache.shape
+    d = x.shape[-1]
+    Hq = sq.shape[0] // D
+    if x.numel() != B * d or q_out.numel() != B * Hq * D or step.numel() != B:
+        raise ValueError("decode_qkv: x, q_out and step must hold B rows")
+    for w_, N in ((wq_packed, Hq * D), (wk_packed, Hkv * D), (wv_packed, Hkv * D)):
+        if w_.numel() != grok_linear_int8_packed_bytes(d, N):
+            raise ValueError("decode_qkv: packed weights do not match the sizes")
+    _check(lib.grok_decode_qkv(_ptr(x), _ptr(gamma), eps, 1 if prenorm else 0, _ptr(wq_packed), _ptr(sq),
+                               _ptr(wk_packed), _ptr(sk), _ptr(wv_packed), _ptr(sv), _ptr(q_out),
+                               _ptr(k_cache), _ptr(v_cache), _ptr(step), _ptr(new_step), _ptr(status),
+                               B, d, Tmax, Hq, Hkv, D, rope_base, _stream(x)), "grok_decode_qkv")
+    return q_out
 
 
 def grok_rope(x, offset=None, base=10000.0):

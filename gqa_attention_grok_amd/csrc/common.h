@@ -69,6 +69,14 @@ hipError_t launch_linear_int8_pack(const int8_t *w, int8_t *wp, int K, int N, hi
 hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
                                    const float *const *scales, void *const *y, const int *N,
                                    int64_t M, int K, hipStream_t s);
+// Decode front half: [norm] -> Q|K|V (packed weights) -> RoPE -> cache slot.
+hipError_t launch_decode_qkv(const void *x, const float *gamma, float eps, bool prenorm,
+                             const int8_t *const *w, const float *const *scales, void *q_out,
+                             void *kc, void *vc, const int32_t *step, int32_t *new_step,
+                             int32_t *status, int B, int d, int Tmax, int Hq, int Hkv,
+                             const RopeFreqs &f, hipStream_t s);
+// Largest B for which the fused pre-norm is available at model width d.
+int decode_qkv_max_prenorm_rows(int d);
 hipError_t launch_prefill_generic(const void *q, const void *k, const void *v, int64_t kv_rows,
                                   const uint8_t *key_valid, void *out, int B, int T, int Hq,
                                   int Hkv, int D, float mult, float cap, int dtype,

@@ -119,6 +119,41 @@ int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w_pack
                     "linear_int8_gemv");
 }
 
+int grok_decode_qkv(const void *x, const float *gamma, float eps, int prenorm,
+                    const int8_t *wq_packed, const float *sq, const int8_t *wk_packed,
+                    const float *sk, const int8_t *wv_packed, const float *sv, void *q_out,
+                    void *k_cache, void *v_cache, const int32_t *step, int32_t *new_step,
+                    int32_t *status, int B, int d, int Tmax, int Hq, int Hkv, int D,
+                    float rope_base, hipStream_t stream) {
+  if (B < 1 || d < 8 || d % 8 || Tmax < 1 || Hq < 1 || Hkv < 1)
+    return fail(GROK_EINVAL, "decode_qkv: bad shape B=%d d=%d Tmax=%d Hq=%d Hkv=%d", B, d, Tmax, Hq, Hkv);
+  if (D != 128) return fail(GROK_EINVAL, "decode_qkv: head size must be 128 (D=%d)", D);
+  if (Hq % Hkv) return fail(GROK_EINVAL, "decode_qkv: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (static_cast<int64_t>(Hq) * D > (1 << 24)) return fail(GROK_EINVAL, "decode_qkv: too many heads");
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return fail(GROK_EINVAL, "decode_qkv: bad rope_base");
+  if (prenorm && (!(eps >= 0.f) || !isfinite(eps))) return fail(GROK_EINVAL, "decode_qkv: bad eps");
+  if (prenorm && B > grok::decode_qkv_max_prenorm_rows(d))
+    return fail(GROK_EINVAL, "decode_qkv: the fused pre-norm takes at most %d rows of width %d (B=%d)",
+                grok::decode_qkv_max_prenorm_rows(d), d, B);
+  if (!x || !wq_packed || !sq || !wk_packed || !sk || !wv_packed || !sv || !q_out || !k_cache || !v_cache || !step)
+    return fail(GROK_EINVAL, "decode_qkv: null pointer");
+  if (new_step && new_step == step) return fail(GROK_EINVAL, "decode_qkv: new_step must not alias step");
+  const uintptr_t a16 = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(wq_packed) |
+                        reinterpret_cast<uintptr_t>(wk_packed) | reinterpret_cast<uintptr_t>(wv_packed);
+  const uintptr_t a4 = reinterpret_cast<uintptr_t>(sq) | reinterpret_cast<uintptr_t>(sk) |
+                       reinterpret_cast<uintptr_t>(sv) | reinterpret_cast<uintptr_t>(gamma);
+  const uintptr_t a2 = reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache);
+  if (a16 % 16 || a4 % 4 || a2 % 2) return fail(GROK_EINVAL, "decode_qkv: misaligned pointer");
+  grok::RopeFreqs f;
+  grok::rope_build_freqs(D, rope_base, &f);
+  const int8_t *w[3] = {wq_packed, wk_packed, wv_packed};
+  const float *sc[3] = {sq, sk, sv};
+  return hip_status(grok::launch_decode_qkv(x, gamma, eps, prenorm != 0, w, sc, q_out, k_cache, v_cache,
+                                            step, new_step, status, B, d, Tmax, Hq, Hkv, f, stream),
+                    "decode_qkv");
+}
+
 int grok_rope(void *x, int B, int T, int H, int D, const int32_t *offset, float base, int dtype,
               hipStream_t stream) {
   if (dtype != GROK_BF16 && dtype != GROK_F32) return fail(GROK_EINVAL, "rope: unknown dtype %d", dtype);

@@ -91,69 +91,30 @@ __device__ __forceinline__ void tie_after_wait(u32x4 *w, u32x4 *x) {
   for (int v = 0; v < NX; ++v) asm volatile("" : "+v"(x[v]));
 }
 
-// MT row tiles of 16 (M <= 16*MT), NB 16-channel blocks per workgroup, W
-// waves, a ring of D steps (one step = one 64-row tile of each block, plus
-// its x unless XL). With XL the M (<= 4) rows of x are first copied to LDS and
-// the A operands read from there.
-template <int MT, int NB, int W, int D, bool XL>
-__global__ __launch_bounds__(W * kWave) void gemv_packed_kernel(GemvArgs a) {
-  constexpr int kLoads = XL ? NB : NB + 2 * MT;  // ring loads per step
+// The product of one wave: tiles [i0, i1) of NB 16-channel blocks (wb[v]
+// points at this lane's 16 bytes of the block's first tile) against MT row
+// tiles of x, accumulated into acc[v][t] (lane: x row 16t + 4g + e, channel
+// i16 of block v). With XL the A operands come from the copy of x in LDS,
+// otherwise they are loaded with the weights.
+//
+// The loads form a ring of D steps, as inline assembly with an explicit wait:
+// when a step is consumed, the (D-1) * kLoads loads of the later steps may
+// still be in flight (loads return in issue order; the compiler's own waits
+// get this count wrong at the loop head). Steps past the range re-read its
+// last tile (a cache hit) and are not consumed.
+template <int MT, int NB, int D, bool XL>
+struct TileRing {
+  static constexpr int kLoads = XL ? NB : NB + 2 * MT;  // load instructions per step
   static_assert((D - 1) * kLoads <= 63, "the wait count must fit vmcnt");
-  static_assert(!XL || MT == 1, "x in LDS is for at most 4 rows");
-  extern __shared__ f32x4 xs4[];  // XL: x rows [M][K] bf16
-  __shared__ float red[W][XL ? 4 : kMaxRows][NB * kTileCols];
-  const int tid = threadIdx.x;
-  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
-  const int M = a.M, K = a.K, KP = a.KP;
-
-  const int b = blockIdx.x;
-  const bool m1 = a.nmat > 1 && b >= a.mat[1].wg0;
-  const bool m2 = a.nmat > 2 && b >= a.mat[2].wg0;
-  const int8_t *w = m2 ? a.mat[2].w : (m1 ? a.mat[1].w : a.mat[0].w);
-  const float *sc = m2 ? a.mat[2].s : (m1 ? a.mat[1].s : a.mat[0].s);
-  bf16_t *y = m2 ? a.mat[2].y : (m1 ? a.mat[1].y : a.mat[0].y);
-  const int N = m2 ? a.mat[2].N : (m1 ? a.mat[1].N : a.mat[0].N);
-  const int j0 = (b - (m2 ? a.mat[2].wg0 : (m1 ? a.mat[1].wg0 : a.mat[0].wg0))) * NB;
-  const int NP = (N + kTileCols - 1) / kTileCols;
-
-  // This wave's tiles: [i0, i1) of every block; blocks past NP re-read block j0.
-  const int i0 = static_cast<int>(static_cast<int64_t>(KP) * wv / W);
-  const int i1 = static_cast<int>(static_cast<int64_t>(KP) * (wv + 1) / W);
-  const int8_t *wb[NB];
-#pragma unroll
-  for (int v = 0; v < NB; ++v)
-    wb[v] = w + (static_cast<int64_t>(j0 + v < NP ? j0 + v : j0) * KP) * kTileBytes + 16 * l;
-  // x rows of this lane (clamped into x; rows >= M are zeroed when consumed)
-  const bf16_t *xr[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) xr[t] = a.x + static_cast<int64_t>(16 * t + i16 < M ? 16 * t + i16 : 0) * K;
-
-  f32x4 acc[NB][MT];
-#pragma unroll
-  for (int v = 0; v < NB; ++v)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[v][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // With XL: x is copied to LDS with loads issued ahead of the ring's, so the
-  // wait below the ring's prologue covers them.
-  constexpr int kStage = XL ? 4 : 1;  // 16-byte x pieces per thread (M*K <= 4*W*64*8)
-  u32x4 st[kStage];
-  const int nst = XL ? M * K / 8 : 0;
-  if constexpr (XL) {
-#pragma unroll
-    for (int r = 0; r < kStage; ++r) {
-      const int c = tid + r * W * kWave;
-      st[r] = load16(a.x + 8 * static_cast<int64_t>(c < nst ? c : 0));
-    }
-  }
-
-  // Ring of D steps, loads as inline assembly with an explicit wait: when a
-  // step is consumed, the (D-1) * kLoads loads of the later steps may still be
-  // in flight (loads return in issue order). Steps past the wave's range
-  // re-read its last tile (a cache hit) and are not consumed.
   u32x4 wr[D][NB];
   u32x4 xa[XL ? 1 : D][MT][2];
-  auto issue = [&](int slot, int i) {
+  const int8_t *wb[NB];
+  const bf16_t *xr[MT];  // this lane's x rows (clamped into x; zeroed past M when used)
+  int i0, i1, K, M, g, i16;
+
+  __device__ __forceinline__ bool busy() const { return i1 > i0; }
+
+  __device__ __forceinline__ void issue(int slot, int i) {
     const int ic = i < i1 ? i : i1 - 1;
 #pragma unroll
     for (int v = 0; v < NB; ++v) wr[slot][v] = load16(wb[v] + static_cast<int64_t>(ic) * kTileBytes);
@@ -166,29 +127,21 @@ __global__ __launch_bounds__(W * kWave) void gemv_packed_kernel(GemvArgs a) {
           xa[slot][t][h] = load16(xr[t] + (k < K ? k : 0));
         }
     }
-  };
-  const bool busy = i1 > i0;
-  if (busy) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) issue(u, i0 + u);
   }
-  if constexpr (XL) {
-    if (busy) {
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(D * kLoads) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+
+  __device__ __forceinline__ void prologue() {
+    if (busy()) {
 #pragma unroll
-    for (int r = 0; r < kStage; ++r) asm volatile("" : "+v"(st[r]));  // uses stay below the wait
-    bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
-#pragma unroll
-    for (int r = 0; r < kStage; ++r) {
-      const int c = tid + r * W * kWave;
-      if (c < nst) *reinterpret_cast<u32x4 *>(xs + 8 * c) = st[r];
+      for (int u = 0; u < D; ++u) issue(u, i0 + u);
     }
-    __syncthreads();
   }
-  if (busy) {
+
+  __device__ __forceinline__ void run(const bf16_t *xs, f32x4 (&acc)[NB][MT]) {
+#pragma unroll
+    for (int v = 0; v < NB; ++v)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[v][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!busy()) return;
     for (int c0 = i0; c0 < i1; c0 += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
@@ -206,13 +159,10 @@ __global__ __launch_bounds__(W * kWave) void gemv_packed_kernel(GemvArgs a) {
             for (int t = 0; t < MT; ++t) {
               const bool ok = kok && 16 * t + i16 < M;
               u32x4 xv;
-              if constexpr (XL) {
-                const bf16_t *xs = reinterpret_cast<const bf16_t *>(xs4);
-                xv = *reinterpret_cast<const u32x4 *>(xs + static_cast<int64_t>(i16 < M ? i16 : 0) * K +
-                                                      (kok ? k : 0));
-              } else {
+              if constexpr (XL)
+                xv = *reinterpret_cast<const u32x4 *>(xs + static_cast<int64_t>(i16 < M ? i16 : 0) * K + (kok ? k : 0));
+              else
                 xv = xa[u][t][h];
-              }
               A[t] = __builtin_bit_cast(bf16x8, ok ? xv : u32x4{0u, 0u, 0u, 0u});
             }
 #pragma unroll
@@ -230,8 +180,158 @@ __global__ __launch_bounds__(W * kWave) void gemv_packed_kernel(GemvArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the unused prefetches
   }
+};
 
-  // acc[v][t][e] = sum for x row 16t + 4g + e, channel 16*(j0+v) + i16.
+// Copy of the M rows of x ([M][K] bf16, M*K <= kStageElems) into LDS, loaded
+// ahead of the ring's prologue and written once the prologue is issued. With
+// kNorm the rows are first normalised as the RMSNorm entry point does
+// (n = bf16(gamma * (x * r)), r = rsqrt(mean(x^2) + eps), fp32 inside).
+constexpr int kStage = 8;  // 16-byte pieces of x per thread
+constexpr int kStageElems = kStage * kThreads * 8;
+
+struct XStage {
+  u32x4 st[kStage];
+  __device__ __forceinline__ void load(const bf16_t *x, int n8) {
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      const int c = threadIdx.x + r * kThreads;
+      st[r] = load16(x + 8 * static_cast<int64_t>(c < n8 ? c : 0));
+    }
+  }
+  // `left` ring loads issued after these may stay in flight.
+  template <int kLeftBusy, bool kNorm>
+  __device__ __forceinline__ void store(bf16_t *xs, bool busy, int M, int K, const float *gamma,
+                                        float eps, float *red /* [kWaves][4] */) {
+    if (busy) {
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLeftBusy) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) asm volatile("" : "+v"(st[r]));  // uses stay below the wait
+    const int n8 = M * K / 8;
+    if constexpr (kNorm) {
+      // per-row sums of squares (a piece lies in one row: K % 8 == 0)
+      float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < kStage; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        if (c < n8) {
+          const int m = 8 * c / K;
+          float part = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float lo = lo_bf16(st[r][q]), hi = hi_bf16(st[r][q]);
+            part += lo * lo;
+            part += hi * hi;
+          }
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+            if (m == mm) ss[mm] += part;
+        }
+      }
+      const int wv = threadIdx.x / kWave;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const float v = wave_sum(ss[mm]);
+        if ((threadIdx.x & (kWave - 1)) == 0) red[wv * 4 + mm] = v;
+      }
+      __syncthreads();
+      float rr[4];
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        float t = 0.f;
+#pragma unroll
+        for (int u = 0; u < kWaves; ++u) t += red[u * 4 + mm];
+        rr[mm] = rsqrtf(t / static_cast<float>(K) + eps);
+      }
+#pragma unroll
+      for (int r = 0; r < kStage; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        if (c < n8) {
+          const int m = 8 * c / K;
+          const int k0 = 8 * c - m * K;
+          const float rm = m == 0 ? rr[0] : m == 1 ? rr[1] : m == 2 ? rr[2] : rr[3];
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float lo = lo_bf16(st[r][q]) * rm, hi = hi_bf16(st[r][q]) * rm;
+            if (gamma) {
+              lo = gamma[k0 + 2 * q] * lo;
+              hi = gamma[k0 + 2 * q + 1] * hi;
+            }
+            o[q] = pack_bf16x2(lo, hi);
+          }
+          *reinterpret_cast<u32x4 *>(xs + 8 * c) = o;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kStage; ++r) {
+        const int c = threadIdx.x + r * kThreads;
+        if (c < n8) *reinterpret_cast<u32x4 *>(xs + 8 * c) = st[r];
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// Matrix of workgroup b (matrices' workgroups are numbered one after another).
+struct MatSel {
+  const int8_t *w;
+  const float *s;
+  bf16_t *y;
+  int N, lw, p;
+  __device__ __forceinline__ MatSel(const GemvArgs &a, int b) {
+    const bool m1 = a.nmat > 1 && b >= a.mat[1].wg0;
+    const bool m2 = a.nmat > 2 && b >= a.mat[2].wg0;
+    p = m2 ? 2 : (m1 ? 1 : 0);
+    w = m2 ? a.mat[2].w : (m1 ? a.mat[1].w : a.mat[0].w);
+    s = m2 ? a.mat[2].s : (m1 ? a.mat[1].s : a.mat[0].s);
+    y = m2 ? a.mat[2].y : (m1 ? a.mat[1].y : a.mat[0].y);
+    N = m2 ? a.mat[2].N : (m1 ? a.mat[1].N : a.mat[0].N);
+    lw = b - (m2 ? a.mat[2].wg0 : (m1 ? a.mat[1].wg0 : a.mat[0].wg0));
+  }
+};
+
+// MT row tiles of 16 (M <= 16*MT), NB consecutive 16-channel blocks per
+// workgroup, a ring of D steps; XL: x (at most 4 rows) copied to LDS first.
+template <int MT, int NB, int D, bool XL>
+__global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
+  static_assert(!XL || MT == 1, "x in LDS is for at most 4 rows");
+  extern __shared__ f32x4 xs4[];  // XL: x rows [M][K] bf16
+  __shared__ float red[kWaves][XL ? 4 : kMaxRows][NB * kTileCols];
+  const int tid = threadIdx.x;
+  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
+  const int M = a.M, K = a.K, KP = a.KP;
+  const MatSel ms(a, blockIdx.x);
+  const int j0 = ms.lw * NB;
+  const int NP = (ms.N + kTileCols - 1) / kTileCols;
+
+  TileRing<MT, NB, D, XL> ring;
+  ring.i0 = static_cast<int>(static_cast<int64_t>(KP) * wv / kWaves);
+  ring.i1 = static_cast<int>(static_cast<int64_t>(KP) * (wv + 1) / kWaves);
+  ring.K = K;
+  ring.M = M;
+  ring.g = g;
+  ring.i16 = i16;
+#pragma unroll
+  for (int v = 0; v < NB; ++v)  // blocks past NP re-read block j0
+    ring.wb[v] = ms.w + (static_cast<int64_t>(j0 + v < NP ? j0 + v : j0) * KP) * kTileBytes + 16 * l;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) ring.xr[t] = a.x + static_cast<int64_t>(16 * t + i16 < M ? 16 * t + i16 : 0) * K;
+
+  XStage xst;
+  if constexpr (XL) xst.load(a.x, M * K / 8);
+  ring.prologue();
+  bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
+  if constexpr (XL)
+    xst.template store<D * TileRing<MT, NB, D, XL>::kLoads, false>(xs, ring.busy(), M, K, nullptr, 0.f,
+                                                                    &red[0][0][0]);
+  f32x4 acc[NB][MT];
+  ring.run(xs, acc);
+
+  __syncthreads();  // red[] may have held the staging sums
 #pragma unroll
   for (int v = 0; v < NB; ++v)
 #pragma unroll
@@ -242,14 +342,125 @@ __global__ __launch_bounds__(W * kWave) void gemv_packed_kernel(GemvArgs a) {
         if (m < M) red[wv][m][kTileCols * v + i16] = acc[v][t][e];
       }
   __syncthreads();
-  for (int q = tid; q < M * NB * kTileCols; q += W * kWave) {
+  for (int q = tid; q < M * NB * kTileCols; q += kThreads) {
     const int m = q / (NB * kTileCols), c = q % (NB * kTileCols);
     const int n = kTileCols * j0 + c;
-    if (n >= N) continue;
+    if (n >= ms.N) continue;
     float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < W; ++u) sum += red[u][m][c];
-    y[static_cast<int64_t>(m) * N + n] = f32_to_bf16(sum * sc[n]);
+    for (int u = 0; u < kWaves; ++u) sum += red[u][m][c];
+    ms.y[static_cast<int64_t>(m) * ms.N + n] = f32_to_bf16(sum * ms.s[n]);
+  }
+}
+
+// Decode front half: Q|K|V projections of one token per sequence (head size
+// 128), with RoPE of q and k at position step[b] and the k, v rows written to
+// cache slot step[b] (ch. 4 §4.4, §4.5.1), optionally normalising x first
+// (kNorm; x then in LDS, at most 4 rows). A workgroup owns the two blocks of
+// 16 channels that RoPE pairs (channels c and c + 64 of a head), so that the
+// rotation happens in its epilogue. The arithmetic after the fp32 sums is the
+// one of the unfused calls: the projection is rounded to bf16, rotated in fp32
+// with the same phase and pinned operations, and rounded again.
+struct QkvArgs {
+  GemvArgs g;    // mat[0] = q (y = q_out), mat[1] = k, mat[2] = v (y unused)
+  bf16_t *kc, *vc;
+  const int32_t *step;
+  int32_t *new_step, *status;
+  const float *gamma;
+  float eps;
+  int Tmax, Hkv;
+  RopeFreqs f;
+};
+
+__device__ __forceinline__ void rope_pair_at(int pos, float inv, float x1, float x2, float &o1, float &o2) {
+  const float theta = __fmul_rn(static_cast<float>(pos), inv);
+  float s, c;
+  sincosf(theta, &s, &c);
+  o1 = __fmaf_rn(x1, c, -__fmul_rn(x2, s));
+  o2 = __fmaf_rn(x2, c, __fmul_rn(x1, s));
+}
+
+template <int MT, int D, bool XL, bool kNorm>
+__global__ __launch_bounds__(kThreads) void decode_qkv_kernel(QkvArgs qa) {
+  constexpr int NB = 2;
+  static_assert(!XL || MT == 1, "x in LDS is for at most 4 rows");
+  static_assert(XL || !kNorm, "the norm needs x in LDS");
+  extern __shared__ f32x4 xs4[];
+  __shared__ float red[kWaves][XL ? 4 : kMaxRows][NB * kTileCols];
+  const GemvArgs &a = qa.g;
+  const int tid = threadIdx.x;
+  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
+  const int M = a.M, K = a.K, KP = a.KP;
+  const MatSel ms(a, blockIdx.x);
+  // blocks (jA, jA + 4) with jA % 8 < 4: channels c and c + 64 of one head
+  const int jA = 8 * (ms.lw / 4) + ms.lw % 4;
+
+  TileRing<MT, NB, D, XL> ring;
+  ring.i0 = static_cast<int>(static_cast<int64_t>(KP) * wv / kWaves);
+  ring.i1 = static_cast<int>(static_cast<int64_t>(KP) * (wv + 1) / kWaves);
+  ring.K = K;
+  ring.M = M;
+  ring.g = g;
+  ring.i16 = i16;
+  ring.wb[0] = ms.w + (static_cast<int64_t>(jA) * KP) * kTileBytes + 16 * l;
+  ring.wb[1] = ms.w + (static_cast<int64_t>(jA + 4) * KP) * kTileBytes + 16 * l;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) ring.xr[t] = a.x + static_cast<int64_t>(16 * t + i16 < M ? 16 * t + i16 : 0) * K;
+
+  XStage xst;
+  if constexpr (XL) xst.load(a.x, M * K / 8);
+  ring.prologue();
+  bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
+  if constexpr (XL)
+    xst.template store<D * TileRing<MT, NB, D, XL>::kLoads, kNorm>(xs, ring.busy(), M, K, qa.gamma, qa.eps,
+                                                                     &red[0][0][0]);
+  f32x4 acc[NB][MT];
+  ring.run(xs, acc);
+
+  __syncthreads();  // red[] may have held the staging sums
+#pragma unroll
+  for (int v = 0; v < NB; ++v)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * t + 4 * g + e;
+        if (m < M) red[wv][m][kTileCols * v + i16] = acc[v][t][e];
+      }
+  __syncthreads();
+  for (int q = tid; q < M * kTileCols; q += kThreads) {
+    const int m = q / kTileCols, c = q % kTileCols;
+    const int nA = kTileCols * jA + c, nB = nA + 64;
+    float sA = 0.f, sB = 0.f;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      sA += red[u][m][c];
+      sB += red[u][m][kTileCols + c];
+    }
+    // the projection as the unfused call hands it on (bf16)
+    const float yA = bf16_to_f32(f32_to_bf16(sA * ms.s[nA]));
+    const float yB = bf16_to_f32(f32_to_bf16(sB * ms.s[nB]));
+    const int pos = qa.step[m];
+    const bool ok = pos >= 0 && pos < qa.Tmax;
+    const int h = nA / 128, i = nA % 128;  // i < 64: nB is its RoPE partner
+    if (ms.p == 0) {  // q: rotated in place of the unfused append, unrotated if skipped
+      float oA = yA, oB = yB;
+      if (ok) rope_pair_at(pos, qa.f.inv[i], yA, yB, oA, oB);
+      ms.y[static_cast<int64_t>(m) * ms.N + nA] = f32_to_bf16(oA);
+      ms.y[static_cast<int64_t>(m) * ms.N + nB] = f32_to_bf16(oB);
+    } else if (ok) {
+      bf16_t *dst = (ms.p == 1 ? qa.kc : qa.vc) + ((static_cast<int64_t>(m) * qa.Tmax + pos) * qa.Hkv + h) * 128;
+      float oA = yA, oB = yB;
+      if (ms.p == 1) rope_pair_at(pos, qa.f.inv[i], yA, yB, oA, oB);
+      dst[i] = f32_to_bf16(oA);
+      dst[i + 64] = f32_to_bf16(oB);
+    }
+  }
+  if (blockIdx.x == 0 && tid < M) {
+    const int pos = qa.step[tid];
+    const bool ok = pos >= 0 && pos < qa.Tmax;
+    if (qa.new_step) qa.new_step[tid] = ok ? pos + 1 : pos;
+    if (!ok && qa.status) *qa.status = GROK_ERANGE;
   }
 }
 
@@ -299,17 +510,17 @@ hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
   for (int64_t r0 = 0; r0 < M; r0 += kMaxRows) {
     const int rows = static_cast<int>(M - r0 < kMaxRows ? M - r0 : kMaxRows);
     // Up to 4 rows: 16 channels per workgroup, x staged in LDS (when it fits
-    // the staging registers, 4 x 16 bytes per thread), 16 steps in flight;
+    // the staging registers, 8 x 16 bytes per thread), 16 steps in flight;
     // up to 16 rows: 32 channels, x from the ring; more: two row tiles.
     int NB = 2;
     bool xl = false;
-    GemvKernel k = gemv_packed_kernel<1, 2, kWaves, 8, false>;
+    GemvKernel k = gemv_packed_kernel<1, 2, 8, false>;
     if (rows > 16) {
-      k = gemv_packed_kernel<2, 2, kWaves, 6, false>;
-    } else if (rows <= 4 && static_cast<int64_t>(rows) * K <= 4 * kThreads * 8) {
+      k = gemv_packed_kernel<2, 2, 6, false>;
+    } else if (rows <= 4 && static_cast<int64_t>(rows) * K <= kStageElems) {
       xl = true;
       NB = 1;
-      k = gemv_packed_kernel<1, 1, kWaves, 16, true>;
+      k = gemv_packed_kernel<1, 1, 16, true>;
     }
     GemvArgs a = {};
     a.x = static_cast<const bf16_t *>(x) + r0 * K;
@@ -330,5 +541,56 @@ hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
   }
   return hipSuccess;
 }
+
+hipError_t launch_decode_qkv(const void *x, const float *gamma, float eps, bool prenorm,
+                             const int8_t *const *w, const float *const *scales, void *q_out,
+                             void *kc, void *vc, const int32_t *step, int32_t *new_step,
+                             int32_t *status, int B, int d, int Tmax, int Hq, int Hkv,
+                             const RopeFreqs &f, hipStream_t stream) {
+  for (int r0 = 0; r0 < B; r0 += kMaxRows) {
+    const int rows = B - r0 < kMaxRows ? B - r0 : kMaxRows;
+    QkvArgs qa = {};
+    GemvArgs &a = qa.g;
+    a.x = static_cast<const bf16_t *>(x) + static_cast<int64_t>(r0) * d;
+    const int Ns[3] = {Hq * 128, Hkv * 128, Hkv * 128};
+    int wg = 0;
+    for (int q = 0; q < 3; ++q) {
+      bf16_t *yq = q == 0 ? static_cast<bf16_t *>(q_out) + static_cast<int64_t>(r0) * Ns[0] : nullptr;
+      a.mat[q] = GemvMat{w[q], scales[q], yq, Ns[q], wg};
+      wg += Ns[q] / 32;  // pairs of 16-channel blocks
+    }
+    a.nmat = 3;
+    a.M = rows;
+    a.K = d;
+    a.KP = (d + kTileRows - 1) / kTileRows;
+    const int64_t slot0 = static_cast<int64_t>(r0) * Tmax * Hkv * 128;
+    qa.kc = static_cast<bf16_t *>(kc) + slot0;
+    qa.vc = static_cast<bf16_t *>(vc) + slot0;
+    qa.step = step + r0;
+    qa.new_step = new_step ? new_step + r0 : nullptr;
+    qa.status = status;
+    qa.gamma = gamma;
+    qa.eps = eps;
+    qa.Tmax = Tmax;
+    qa.Hkv = Hkv;
+    qa.f = f;
+    const bool xl = rows <= 4 && static_cast<int64_t>(rows) * d <= kStageElems;
+    if (prenorm && !xl) return hipErrorInvalidValue;  // validated by the caller
+    void (*k)(QkvArgs);
+    if (xl)
+      k = prenorm ? decode_qkv_kernel<1, 16, true, true> : decode_qkv_kernel<1, 16, true, false>;
+    else if (rows <= 16)
+      k = decode_qkv_kernel<1, 8, false, false>;
+    else
+      k = decode_qkv_kernel<2, 6, false, false>;
+    const size_t lds = xl ? static_cast<size_t>(rows) * d * 2 : 0;
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wg)), dim3(kThreads), lds, stream, qa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+int decode_qkv_max_prenorm_rows(int d) { return d > 0 ? (kStageElems / d < 4 ? kStageElems / d : 4) : 0; }
 
 }  // namespace grok

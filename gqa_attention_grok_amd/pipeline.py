@@ -22,8 +22,8 @@ from __future__ import annotations
 import torch
 
 from . import (grok_attn_decode, grok_attn_decode_workspace_bytes, grok_attn_prefill,
-               grok_kv_append, grok_linear_int8, grok_linear_int8_gemv, grok_linear_int8_pack,
-               grok_rmsnorm, grok_rope)
+               grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
+               grok_linear_int8_pack, grok_rmsnorm, grok_rope)
 
 
 def capture(step) -> "torch.cuda.CUDAGraph":
@@ -130,8 +130,11 @@ class DecodeSublayerStep:
     product streams."""
 
     def __init__(self, x, k_cache, v_cache, step, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D,
-                 attn_mult, softcap=30.0, eps=1e-5, rope_base=10000.0):
+                 attn_mult, softcap=30.0, eps=1e-5, rope_base=10000.0, fused=True):
         self.x, self.k_cache, self.v_cache, self.step = x, k_cache, v_cache, step
+        self.fused = fused
+        # the fused pre-norm keeps x on chip: up to 4 rows of up to 8192 values in all
+        self.max_prenorm_rows = min(4, 32768 // x.shape[-1])
         self.packed = tuple(grok_linear_int8_pack(w_) for w_ in (wq, wk, wv, wo))
         self.scales = (sq, sk, sv, so)
         self.attn_mult, self.softcap, self.eps, self.rope_base = attn_mult, softcap, eps, rope_base
@@ -159,11 +162,27 @@ class DecodeSublayerStep:
     def project_out(self):
         grok_linear_int8_gemv(self.attn, [self.packed[3]], [self.scales[3]], [self.o])
 
+    def front(self):
+        """norm -> Q|K|V -> RoPE -> cache slot. Fused into one launch (the norm
+        too when the rows fit on chip); unfused: norm, projection, append."""
+        pq, pk, pv, _ = self.packed
+        sq, sk, sv, _ = self.scales
+        if self.fused:
+            B = self.x.shape[0]
+            prenorm = B <= self.max_prenorm_rows
+            if not prenorm:
+                grok_rmsnorm(self.x, self.n, eps=self.eps)
+            grok_decode_qkv(self.x if prenorm else self.n, pq, sq, pk, sk, pv, sv, self.q, self.k_cache,
+                            self.v_cache, self.step, new_step=self.kv_len, status=self.status,
+                            prenorm=prenorm, eps=self.eps, rope_base=self.rope_base)
+        else:
+            grok_rmsnorm(self.x, self.n, eps=self.eps)
+            self.project_qkv()
+            grok_kv_append(self.k_cache, self.v_cache, self.k, self.v, self.step, q_inout=self.q,
+                           new_step=self.kv_len, status=self.status, rope_base=self.rope_base)
+
     def __call__(self):
-        grok_rmsnorm(self.x, self.n, eps=self.eps)
-        self.project_qkv()
-        grok_kv_append(self.k_cache, self.v_cache, self.k, self.v, self.step, q_inout=self.q,
-                       new_step=self.kv_len, status=self.status, rope_base=self.rope_base)
+        self.front()
         grok_attn_decode(self.q, self.k_cache, self.v_cache, self.kv_len, self.attn, self.attn_ws,
                          self.attn_mult, self.softcap, status=self.status)
         self.project_out()

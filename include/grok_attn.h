@@ -126,6 +126,37 @@ GROK_API int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *cons
                                    int64_t M, int K, hipStream_t stream);
 
 /*
+ * Front half of the attention sub-layer for one new token per sequence
+ * ([ch6] §6.3.1 pre-norm, [ch4] §4.5.1 projections, §4.3.1 RoPE, §4.4
+ * RoPE-then-cache), in one launch: with p = step[b],
+ *   n        = prenorm ? rmsnorm(x; gamma, eps) rounded to bf16 : x
+ *   q_out[b] = rope(bf16(n[b] @ Wq * sq), p)                       (bf16)
+ *   k_cache[b, p] = rope(bf16(n[b] @ Wk * sk), p),  v_cache[b, p] = bf16(n[b] @ Wv * sv)
+ *   new_step[b] = p + 1                                 (if new_step is not NULL)
+ * with the same arithmetic (and, for a given n, the same bits) as
+ * grok_linear_int8_gemv followed by grok_kv_append(q_inout = q_out); the
+ * fused norm sums squares in another order than grok_rmsnorm, so n may
+ * differ from it by one bf16 rounding.
+ *   x        [B, d] bf16; gamma [d] fp32 or NULL (unit scale), used with prenorm.
+ *   w*_packed  grok_linear_int8_pack of Wq [d, Hq*128], Wk, Wv [d, Hkv*128];
+ *   s*       their fp32 channel scales; q_out [B, Hq*128] bf16 (must not overlap x).
+ *   caches   [B, Tmax, Hkv, 128] bf16; step [B] int32 device, new_step [B]
+ *            int32 device or NULL (must not alias step); status as for
+ *            grok_kv_append: a sequence with step[b] outside [0, Tmax) gets
+ *            no cache write, its unrotated q row, new_step[b] = step[b], and
+ *            GROK_ERANGE is stored to *status.
+ * Errors: EINVAL for NULL pointers, sizes < 1, d not a multiple of 8, D !=
+ * 128, Hq % Hkv != 0, bad rope_base or eps, misaligned pointers, new_step ==
+ * step, or prenorm with B above what fits on chip (4 rows of width <= 8192).
+ */
+GROK_API int grok_decode_qkv(const void *x, const float *gamma, float eps, int prenorm,
+                             const int8_t *wq_packed, const float *sq, const int8_t *wk_packed,
+                             const float *sk, const int8_t *wv_packed, const float *sv,
+                             void *q_out, void *k_cache, void *v_cache, const int32_t *step,
+                             int32_t *new_step, int32_t *status, int B, int d, int Tmax, int Hq,
+                             int Hkv, int D, float rope_base, hipStream_t stream);
+
+/*
  * Rotary embedding, in place ([ch4] §4.3, §4.3.1): for x [B, T, H, D] and the
  * position p = offset[b] + t,
  *   inv_freq[i] = base^(-2i/D) (fp32),  theta_i = fp32(p * inv_freq[i]),

@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 14, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -197,3 +197,27 @@ def test_pack_and_gemv_validation(lib):
     assert call(n_mats=2, N=Ns(6144, 1024), w=arr(0x10000, None, 0x10000)) == EINVAL
     assert call(M=-1) == EINVAL
     assert call(M=0, x=None) == 0
+
+
+def test_decode_qkv_validation(lib):
+    f = lib.grok_decode_qkv
+    f.restype = ctypes.c_int
+
+    def call(x=FAKE, prenorm=0, B=1, d=6144, Tmax=8192, Hq=48, Hkv=8, D=128, base=1e4, eps=1e-5,
+             step=FAKE, new_step=ctypes.c_void_p(0x20000), q=FAKE):
+        return f(x, None, fl(eps), i(prenorm), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, q, FAKE, FAKE, step,
+                 new_step, None, i(B), i(d), i(Tmax), i(Hq), i(Hkv), i(D), fl(base), None)
+    assert call(D=64) == EINVAL
+    assert call(Hq=44) == EINVAL
+    assert call(d=6140) == EINVAL
+    assert call(base=0.0) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(step=None) == EINVAL
+    assert call(new_step=FAKE) == EINVAL                   # aliases step
+    assert call(x=ctypes.c_void_p(0x10008)) == EINVAL      # x 16-byte alignment
+    assert call(q=ctypes.c_void_p(0x10001)) == EINVAL      # bf16 alignment
+    assert call(prenorm=1, B=5) == EINVAL                  # the fused norm keeps <= 4 rows on chip
+    assert "at most 4 rows" in _err(lib)
+    assert call(prenorm=1, B=4, d=16384) == EINVAL         # 4 x 16384 values do not fit either
+    assert "at most 2 rows" in _err(lib)
+    assert call(prenorm=1, B=1, eps=-1.0) == EINVAL

@@ -421,15 +421,107 @@ def test_decode_bad_lengths_give_zero_rows_and_status(G):
     U.assert_bf16_close(got[1:2], ref, "valid row next to bad ones")
 
 
+@pytest.mark.parametrize("B,d,Hq,Hkv,Tmax", [
+    (1, 256, 4, 2, 300),
+    (3, 1024, 8, 1, 64),      # x staged on chip (3 x 1024 values)
+    (5, 256, 4, 2, 40),       # more rows than the on-chip path takes
+    (20, 512, 16, 2, 33),     # two row tiles
+])
+def test_decode_qkv_matches_unfused_calls(G, B, d, Hq, Hkv, Tmax):
+    """Projection + RoPE + cache write in one launch give the bits of the
+    separate calls (few-row projection, then append with q in place)."""
+    grok, U, torch = G
+    D = 128
+    g = gi.rng(B * 1000 + d)
+    xb = gi.normal_bf16(g, (B, d))
+    ws = [gi.int8_uniform(g, (d, n)) for n in (Hq * D, Hkv * D, Hkv * D)]
+    ss = [(0.02 / 127 * g.uniform(0.5, 1.5, n)).astype(np.float32) for n in (Hq * D, Hkv * D, Hkv * D)]
+    steps = g.integers(0, Tmax, size=B).astype(np.int32)
+    steps[0] = Tmax - 1
+    if B > 2:
+        steps[1] = Tmax   # out of range: skipped
+    kc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    vc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    x = U.dev_bf16(xb)
+    wp = [grok.grok_linear_int8_pack(U.dev(w)) for w in ws]
+    ds = [U.dev(s_) for s_ in ss]
+    stp = U.dev(steps)
+    # unfused
+    q1 = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
+    k1 = torch.empty((B, 1, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v1 = torch.empty_like(k1)
+    kc1, vc1 = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    ns1 = torch.empty(B, dtype=torch.int32, device="cuda")
+    st1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grok.grok_linear_int8_gemv(x, wp, ds, [q1, k1, v1])
+    grok.grok_kv_append(kc1, vc1, k1, v1, stp, q_inout=q1, new_step=ns1, status=st1)
+    # fused
+    q2 = torch.empty((B, Hq * D), dtype=torch.bfloat16, device="cuda")
+    kc2, vc2 = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    ns2 = torch.empty(B, dtype=torch.int32, device="cuda")
+    st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grok.grok_decode_qkv(x, wp[0], ds[0], wp[1], ds[1], wp[2], ds[2], q2, kc2, vc2, stp, new_step=ns2,
+                         status=st2)
+    torch.cuda.synchronize()
+    ok = steps < Tmax
+    # q: rotated where the append ran; where it was skipped, both hold the projection
+    np.testing.assert_array_equal(U.bits(q2).reshape(B, Hq, D)[ok], U.bits(q1).reshape(B, Hq, D)[ok])
+    np.testing.assert_array_equal(U.bits(kc2), U.bits(kc1))
+    np.testing.assert_array_equal(U.bits(vc2), U.bits(vc1))
+    np.testing.assert_array_equal(ns2.cpu().numpy(), ns1.cpu().numpy())
+    assert st2.item() == st1.item() == (0 if ok.all() else -34)
+    if not ok.all():
+        np.testing.assert_array_equal(U.bits(q2).reshape(B, Hq, D)[~ok], U.bits(q1).reshape(B, Hq, D)[~ok])
+
+
+@pytest.mark.parametrize("B,d,gamma", [(1, 6144, False), (2, 6144, True), (4, 1024, True)])
+def test_decode_qkv_fused_norm(G, B, d, gamma):
+    """With the pre-norm fused, against the oracle: norm, projections, RoPE at
+    step[b], the cache slot written and no other."""
+    grok, U, torch = G
+    Hq, Hkv, D, Tmax = 4, 2, 128, 50
+    g = gi.rng(B + d)
+    xb = gi.normal_bf16(g, (B, d))
+    gm = (g.uniform(0.5, 1.5, d)).astype(np.float32) if gamma else None
+    ws = [gi.int8_uniform(g, (d, n)) for n in (Hq * D, Hkv * D, Hkv * D)]
+    ss = [(0.02 / 127 * g.uniform(0.5, 1.5, n)).astype(np.float32) for n in (Hq * D, Hkv * D, Hkv * D)]
+    steps = g.integers(0, Tmax, size=B).astype(np.int32)
+    kc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    vc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    wp = [grok.grok_linear_int8_pack(U.dev(w)) for w in ws]
+    ds = [U.dev(s_) for s_ in ss]
+    q = torch.empty((B, Hq * D), dtype=torch.bfloat16, device="cuda")
+    kc, vc = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    grok.grok_decode_qkv(U.dev_bf16(xb), wp[0], ds[0], wp[1], ds[1], wp[2], ds[2], q, kc, vc, U.dev(steps),
+                         prenorm=True, gamma=None if gm is None else U.dev(gm))
+    x64 = orc.bf16_bits_to_f64(xb)
+    n = orc.rmsnorm(x64, gm, 1e-5, out="bf16")
+    pos = steps.reshape(B, 1).astype(np.int64)
+    qr = orc.rope(orc.linear_int8(n, ws[0], ss[0], out="bf16").reshape(B, 1, Hq, D), pos)
+    kr = orc.rope(orc.linear_int8(n, ws[1], ss[1], out="bf16").reshape(B, 1, Hkv, D), pos)
+    vr = orc.linear_int8(n, ws[2], ss[2]).reshape(B, Hkv, D)
+    U.assert_bf16_close(U.host(q).reshape(B, 1, Hq, D), qr, "fused q")
+    kch, vch = U.host(kc), U.host(vc)
+    for b in range(B):
+        U.assert_bf16_close(kch[b, steps[b]], kr[b, 0], f"fused k slot b={b}")
+        U.assert_bf16_close(vch[b, steps[b]], vr[b], f"fused v slot b={b}")
+    mask = np.ones((B, Tmax), bool)
+    mask[np.arange(B), steps] = False
+    np.testing.assert_array_equal(U.bits(kc)[mask], kc0[mask])
+    np.testing.assert_array_equal(U.bits(vc)[mask], vc0[mask])
+
+
 # --------------------------------------------------------------------------
 # Decode-time sub-layer (norm, few-row projections, RoPE + append, decode
 # attention, output projection, post-norm + residual)
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("B,d,Hq,Hkv,lens,Tmax", [
-    (3, 256, 4, 2, [300, 77, 1], 300),   # full, short and single-slot memories
-    (2, 1024, 16, 2, [129, 1000], 1024),  # 8 query heads per KV head
+@pytest.mark.parametrize("B,d,Hq,Hkv,lens,Tmax,fused", [
+    (3, 256, 4, 2, [300, 77, 1], 300, True),    # full, short and single-slot memories
+    (3, 256, 4, 2, [300, 77, 1], 300, False),   # the same through separate calls
+    (2, 1024, 16, 2, [129, 1000], 1024, True),  # 8 query heads per KV head
+    (6, 256, 4, 2, [5, 6, 7, 8, 9, 10], 16, True),  # pre-norm not fused (more rows than on chip)
 ])
-def test_decode_sublayer(G, B, d, Hq, Hkv, lens, Tmax):
+def test_decode_sublayer(G, B, d, Hq, Hkv, lens, Tmax, fused):
     grok, U, torch = G
     import gqa_attention_grok_amd.pipeline as pipe
     D, mult = 128, 1 / math.sqrt(128)
@@ -438,7 +530,7 @@ def test_decode_sublayer(G, B, d, Hq, Hkv, lens, Tmax):
     dv = {k: (U.dev_bf16(v) if v.dtype == np.uint16 else U.dev(v)) for k, v in p.items()}
     st = pipe.DecodeSublayerStep(dv["x"], dv["k_cache"], dv["v_cache"], dv["step"], dv["wq"], dv["sq"],
                                  dv["wk"], dv["sk"], dv["wv"], dv["sv"], dv["wo"], dv["so"], Hq, Hkv, D,
-                                 mult)
+                                 mult, fused=fused)
     y = U.host(st())
     torch.cuda.synchronize()
     assert st.status.item() == 0
