@@ -190,13 +190,14 @@ def bench_decode_sublayer(torch, grok, pipe, U, gi, name, steps, warmup, replica
     graphs = [pipe.capture(s_) for s_ in steps_obj]
     sec = time_replays(torch, graphs, steps, warmup)
 
-    # both few-row projections of one step, replayed from graphs (no host work)
-    pgraphs = [pipe.capture(lambda s_=s_: (s_.project_qkv(), s_.project_out())) for s_ in steps_obj]
+    # the weight-streaming kernels of one step (norm + Q|K|V + RoPE + append, and
+    # the output projection), replayed from graphs (no host work)
+    pgraphs = [pipe.capture(lambda s_=s_: (s_.front(), s_.project_out())) for s_ in steps_obj]
     proj_ms = time_replays(torch, pgraphs, steps, warmup) * 1e3
     pbytes = d * cols + Hq * D * d + 4 * (cols + d) + B * 2 * (d + cols + Hq * D + d)
     return {
         "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",
-        "bytes_per_step": nbytes, "kernel": "gemv_packed_kernel (Q|K|V and O projections)",
+        "bytes_per_step": nbytes, "kernel": "decode_qkv_kernel + gemv_packed_kernel (Q|K|V with norm/RoPE/append, O)",
         "kernel_ms": proj_ms, "kernel_gbs": pbytes / (proj_ms * 1e-3) / 1e9,
         "kernel_frac_of_hbm_peak": pbytes / (proj_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "replicas": replicas,
