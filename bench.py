@@ -68,17 +68,39 @@ def traffic_for(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def time_replays(torch, graphs, steps, warmup):
-    """Warm up, then time `steps` replays (cycling over `graphs`) between two
-    device synchronisations; returns seconds per step."""
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+def steps_per_graph(steps):
+    """Steps captured per graph: 8 (or the largest of 4, 2, 1 dividing `steps`),
+    so that exactly `steps` steps are timed and the host's graph launches do
+    not pace a step of a few tens of microseconds."""
+    for k in (8, 4, 2, 1):
+        if steps % k == 0:
+            return k
+    return 1
+
+
+def time_steps(torch, pipe, fns, steps, warmup):
+    """Capture consecutive steps (cycling over `fns`, e.g. one per replica of the
+    inputs) into HIP graphs of steps_per_graph(steps) steps each, warm up, then
+    time exactly `steps` steps between two device synchronisations; returns
+    seconds per step."""
+    k = steps_per_graph(steps)
+    R = len(fns)
+    ngraphs = R // math.gcd(R, k)  # graphs until the replica cycle repeats
+    graphs = []
+    for gi_ in range(ngraphs):
+        idx = [(gi_ * k + j) % R for j in range(k)]
+        graphs.append(pipe.capture(lambda idx=idx: [fns[i]() for i in idx]))
+    nrep = steps // k
+    for i in range(max(1, warmup // k)):
+        graphs[i % ngraphs].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    for i in range(nrep):
+        graphs[i % ngraphs].replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    sec = (time.perf_counter() - t0) / (nrep * k)
+    del graphs
+    return sec
 
 
 def time_kernel(torch, fn, reps):
@@ -103,8 +125,7 @@ def bench_prefill(torch, grok, pipe, U, gi, steps, warmup):
                           w.softcap)
     del p
     flop = 4 * w.D * w.Hq * w.B * w.T * (w.T + 1) // 2
-    g = pipe.capture(st)
-    sec = time_replays(torch, [g], steps, warmup)
+    sec = time_steps(torch, pipe, [st], steps, warmup)
     kern_ms = time_kernel(torch, lambda i: st.attend(), max(steps, 5))
     return {
         "workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12, "unit": "TFLOP/s",
@@ -114,7 +135,8 @@ def bench_prefill(torch, grok, pipe, U, gi, steps, warmup):
 
 
 def bench_decode(torch, grok, pipe, U, gi, name, steps, warmup, replicas):
-    """One step = RoPE + append of the new token, then split-K decode attention.
+    """One step = RoPE + append of the new token and split-K decode attention (the
+    append runs inside the split kernel), then the combine.
     `replicas` copies of the cache are cycled so the working set exceeds the
     256 MB last-level cache and each step streams K/V from HBM."""
     w = gi.WORKLOADS[name]
@@ -129,18 +151,15 @@ def bench_decode(torch, grok, pipe, U, gi, name, steps, warmup, replicas):
     kv_bytes = int(L.sum()) * Hkv * D * 2 * 2
     io_bytes = w.B * (Hq * D * 2 + 2 * Hkv * D * 2 + Hq * D * 2)
     nbytes = kv_bytes + io_bytes
-    graphs = [pipe.capture(s_) for s_ in steps_obj]
-    sec = time_replays(torch, graphs, steps, warmup)
+    sec = time_steps(torch, pipe, steps_obj, steps, warmup)
 
-    def attend(i):
-        s_ = steps_obj[i % len(steps_obj)]
-        grok.grok_attn_decode(s_.q, s_.k_cache, s_.v_cache, s_.kv_len, s_.out, s_.workspace,
-                              s_.attn_mult, s_.softcap, status=s_.status)
+    def attend(i):  # the step's launches, eager (split with the append fused, combine)
+        steps_obj[i % len(steps_obj)]()
 
     kern_ms = time_kernel(torch, attend, max(steps, 2 * len(steps_obj)))
     return {
         "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",
-        "bytes_per_step": nbytes, "kernel": "decode_split_kernel+decode_combine_kernel",
+        "bytes_per_step": nbytes, "kernel": "decode_split_kernel(append fused)+decode_combine_kernel",
         "kernel_ms": kern_ms, "kernel_gbs": nbytes / (kern_ms * 1e-3) / 1e9,
         "kernel_frac_of_hbm_peak": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "cache_replicas": replicas,
@@ -158,7 +177,7 @@ def bench_sublayer(torch, grok, pipe, U, gi, steps, warmup):
     proj = 2 * M * d * (w.Hq * w.D + 2 * w.Hkv * w.D) + 2 * M * (w.Hq * w.D) * d
     attn = 4 * w.D * w.Hq * w.B * w.T * (w.T + 1) // 2
     flop = proj + attn
-    sec = time_replays(torch, [pipe.capture(st)], steps, warmup)
+    sec = time_steps(torch, pipe, [st], steps, warmup)
     return {"workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12,
             "unit": "TFLOP/s", "flop_per_step": flop}
 
@@ -187,13 +206,12 @@ def bench_decode_sublayer(torch, grok, pipe, U, gi, name, steps, warmup, replica
     kv_bytes = int(L.sum()) * Hkv * D * 2 * 2               # valid K and V slots, once
     io_bytes = B * (2 * d * 2 + 2 * Hkv * D * 2)            # x in, y out, new k/v written
     nbytes = w_bytes + kv_bytes + io_bytes
-    graphs = [pipe.capture(s_) for s_ in steps_obj]
-    sec = time_replays(torch, graphs, steps, warmup)
+    sec = time_steps(torch, pipe, steps_obj, steps, warmup)
 
     # the weight-streaming kernels of one step (norm + Q|K|V + RoPE + append, and
     # the output projection), replayed from graphs (no host work)
-    pgraphs = [pipe.capture(lambda s_=s_: (s_.front(), s_.project_out())) for s_ in steps_obj]
-    proj_ms = time_replays(torch, pgraphs, steps, warmup) * 1e3
+    proj_ms = time_steps(torch, pipe, [lambda s_=s_: (s_.front(), s_.project_out()) for s_ in steps_obj],
+                         steps, warmup) * 1e3
     pbytes = d * cols + Hq * D * d + 4 * (cols + d) + B * 2 * (d + cols + Hq * D + d)
     return {
         "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",

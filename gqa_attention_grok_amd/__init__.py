@@ -22,7 +22,8 @@ __all__ = [
     "grok_abi_version", "grok_status_string", "grok_last_error",
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
     "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
-    "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_workspace_bytes",
+    "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_append",
+    "grok_attn_decode_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrokattn.so")
@@ -53,6 +54,8 @@ _PROTOS = {
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
     "grok_attn_decode": (_i, [_p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i, _f, _f, _p]),
     "grok_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "grok_attn_decode_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i,
+                                     _f, _f, _f, _p]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _fn = getattr(lib, _name)
@@ -278,4 +281,29 @@ def grok_attn_decode(q, k_cache, v_cache, kv_len, out, workspace, attn_mult, sof
     _check(lib.grok_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(out),
                                 _ptr(workspace), ws_bytes, _ptr(status), B, Tmax, Hq, Hkv, D,
                                 attn_mult, softcap, _stream(q)), "grok_attn_decode")
+    return out
+
+
+def grok_attn_decode_append(q, k_new, v_new, k_cache, v_cache, step, out, workspace, attn_mult,
+                            softcap=30.0, new_step=None, q_out=None, status=None, rope_base=10000.0):
+    """RoPE q and the new k at step[b], write k/v to slot step[b], attend slots
+    [0, step[b]]: one decode step in one call (q itself is not modified)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_new, "k_new", torch.bfloat16, 4)
+    _need(v_new, "v_new", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(step, "step", torch.int32, 1)
+    _need(out, "out", torch.bfloat16)
+    _need(workspace, "workspace")
+    _need(new_step, "new_step", torch.int32, 1)
+    _need(q_out, "q_out", torch.bfloat16)
+    _need(status, "status", torch.int32)
+    B, _, Hq, D = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.grok_attn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(step), _ptr(new_step), _ptr(q_out), _ptr(out), _ptr(workspace),
+                                       ws_bytes, _ptr(status), B, Tmax, Hq, Hkv, D, attn_mult, softcap,
+                                       rope_base, _stream(q)), "grok_attn_decode_append")
     return out

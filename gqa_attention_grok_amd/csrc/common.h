@@ -36,6 +36,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// RoPE of one pair at integer position `pos` (ch. 4 §4.3.1): the phase is the
+// fp32 product pos * inv_freq, cos/sin are the accurate library functions, and
+// every rounding step is pinned (no contraction), so that every kernel that
+// rotates produces the same bits.
+__device__ __forceinline__ void rope_phase(int pos, float inv, float &s, float &c) {
+  const float theta = __fmul_rn(static_cast<float>(pos), inv);
+  sincosf(theta, &s, &c);
+}
+__device__ __forceinline__ void rope_rotate(float x1, float x2, float c, float s, float &o1, float &o2) {
+  o1 = __fmaf_rn(x1, c, -__fmul_rn(x2, s));
+  o2 = __fmaf_rn(x2, c, __fmul_rn(x1, s));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -89,5 +102,9 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
                          void *out, void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,
                          float mult, float cap, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv);
+hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, void *kc, void *vc,
+                                const int32_t *step, int32_t *new_step, void *q_out, void *out,
+                                void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,
+                                float mult, float cap, const RopeFreqs &f, hipStream_t st);
 
 }  // namespace grok

@@ -26,6 +26,16 @@
 // split is written.
 // Kernel 2 (decode_combine_kernel): one workgroup per (sequence, query head)
 // adds the partials of the splits and writes bf16 sum(p*v) / sum(p).
+//
+// With the append fused (decode_split_kernel<true>, §4.4: RoPE before the
+// cache write), the new token's position is step[b] and the cache holds slots
+// [0, step[b]) only: every workgroup rotates its query heads in registers
+// (the rotation pairs dims i and i + 64, which one lane holds together), the
+// workgroup whose split contains slot step[b] takes that slot's K row from
+// the new k (rotated the same way) and its V row from the new v, and writes
+// both into the cache. The rotation is rope_rotate of common.h at the phases
+// of rope_phase, rounded to bf16 as the unfused append rounds it, so the
+// results are those of the separate append + decode calls.
 #include "attn_tile.h"
 
 namespace grok {
@@ -47,14 +57,41 @@ struct DecodeArgs {
   int32_t *status;
   int B, Tmax, Hq, Hkv, G, S, split_keys;
   float k1, k2inv;
+  // fused append: q is unrotated, len = step[b] + 1
+  const bf16_t *kn, *vn;  // [B, Hkv, D] new k (unrotated), v
+  bf16_t *kcw, *vcw;      // the caches, written at slot step[b]
+  const int32_t *step;
+  int32_t *new_step;      // or NULL
+  bf16_t *q_out;          // rotated q, or NULL
+  float inv[kD / 2];      // RoPE inv_freq
 };
 
+// Rotate the 8 bf16 pairs (x1 in w1, x2 in w2, element e <-> dim i0 + e and
+// i0 + e + 64) with the cos/sin table, rounding to bf16.
+__device__ __forceinline__ void rope8(u32x4 &w1, u32x4 &w2, const float *cs, const float *sn) {
+  u32x4 o1, o2;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a0, a1, b0, b1;
+    rope_rotate(lo_bf16(w1[q]), lo_bf16(w2[q]), cs[2 * q], sn[2 * q], a0, b0);
+    rope_rotate(hi_bf16(w1[q]), hi_bf16(w2[q]), cs[2 * q + 1], sn[2 * q + 1], a1, b1);
+    o1[q] = pack_bf16x2(a0, a1);
+    o2[q] = pack_bf16x2(b0, b1);
+  }
+  w1 = o1;
+  w2 = o2;
+}
+
+template <bool kAppend>
 __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[kSplit * kRowBytes];
   __shared__ float red_l[kSplitWaves][16];
+  __shared__ __attribute__((aligned(16))) float rcs[kAppend ? kD / 2 : 1], rsn[kAppend ? kD / 2 : 1];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int len = a.kv_len[b];
+  const int len = kAppend ? a.step[b] + 1 : a.kv_len[b];
+  if (kAppend && s == 0 && g == 0 && threadIdx.x == 0 && a.new_step)
+    a.new_step[b] = (len >= 1 && len <= a.Tmax) ? len : len - 1;
   if (len < 1 || len > a.Tmax) return;  // reported by the combine kernel
   const int sbase = s * kSplit;
   if (sbase >= len) return;  // whole workgroup: no barrier is skipped
@@ -72,10 +109,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   // (slot R), lane L writing physical chunk L%16. Slots past the sequence read
   // its last slot (masked below). The register loads are inline assembly and
   // issued first, so one explicit wait (vmcnt(8)) makes Q and K usable while
-  // the eight V loads stay in flight.
+  // the eight V loads stay in flight. With the append fused, slot `last`
+  // (and the clamped slots past it) reads the new k / v rows instead.
   const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
   const bf16_t *kbase = a.kc + (static_cast<int64_t>(b) * a.Tmax * a.Hkv + g) * kD;
   const bf16_t *vbase = a.vc + (static_cast<int64_t>(b) * a.Tmax * a.Hkv + g) * kD;
+  const int64_t nrow = (static_cast<int64_t>(b) * a.Hkv + g) * kD;  // new k / v row
   const bool qok = lr < a.G;
   u32x4 qw[4], kf[2][4];
   {
@@ -83,10 +122,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qw[kk]) : "v"(qp + 32 * kk + 8 * lg) : "memory");
   }
+  bool knew[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int kj = min(sbase + 32 * wave + k_row_key(16 * kb + lr), last);
-    const bf16_t *kp = kbase + kj * rstride + 8 * lg;
+    knew[kb] = kAppend && kj == last;
+    const bf16_t *kp = (knew[kb] ? a.kn + nrow : kbase + kj * rstride) + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kf[kb][kk]) : "v"(kp + 32 * kk) : "memory");
   }
@@ -96,9 +137,23 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
     for (int j = 0; j < 8; ++j) {
       const int R = 32 * wave + 4 * j + lrow;
       const int vj = min(sbase + R, last);
-      __builtin_amdgcn_global_load_lds(vbase + vj * rstride + 8 * (lchunk ^ v_swz(R)),
+      const bf16_t *vrow = (kAppend && vj == last) ? a.vn + nrow : vbase + vj * rstride;
+      __builtin_amdgcn_global_load_lds(vrow + 8 * (lchunk ^ v_swz(R)),
                                        (lds_void *)(&Vs[(32 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
     }
+  }
+  if constexpr (kAppend) {
+    // cos/sin of the new position, once per workgroup, while the loads fly
+    // (the table is read with uniform indices: scalar loads, which do not
+    // count against the vector-memory wait below)
+    float inv = 0.f;
+#pragma unroll
+    for (int i = 0; i < kD / 2; ++i) inv = threadIdx.x == i ? a.inv[i] : inv;
+    if (threadIdx.x < kD / 2) rope_phase(last, inv, rsn[threadIdx.x], rcs[threadIdx.x]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // Workgroup barrier without a memory fence (a fence would wait for the
+    // loads in flight); the memory clobber keeps the table reads below it.
+    asm volatile("s_barrier" ::: "memory");
   }
 
   asm volatile("s_waitcnt vmcnt(8)"
@@ -106,6 +161,36 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
                  "+v"(kf[0][3]), "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(kf[1][2]), "+v"(kf[1][3])
                :
                : "memory");
+  if constexpr (kAppend) {
+    // lane (lr, lg) holds dims 32*kk + 8*lg + e of its rows: kk = 0, 1 pair
+    // with kk = 2, 3 (dim + 64)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float cs[8], sn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cs[e] = rcs[32 * kk + 8 * lg + e];
+        sn[e] = rsn[32 * kk + 8 * lg + e];
+      }
+      rope8(qw[kk], qw[kk + 2], cs, sn);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (knew[kb]) rope8(kf[kb][kk], kf[kb][kk + 2], cs, sn);
+    }
+    // the rotated q (split 0) and the rotated new k row (its own slot) out
+    if (s == 0 && qok && a.q_out) {
+      bf16_t *qo = a.q_out + (static_cast<int64_t>(b) * a.Hq + g * a.G + lr) * kD + 8 * lg;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4 *>(qo + 32 * kk) = qw[kk];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (knew[kb] && sbase + 32 * wave + k_row_key(16 * kb + lr) == last) {
+        bf16_t *ko = a.kcw + (static_cast<int64_t>(b) * a.Tmax + last) * rstride + g * kD + 8 * lg;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4 *>(ko + 32 * kk) = kf[kb][kk];
+      }
+  }
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, qok ? qw[kk] : u32x4{0, 0, 0, 0});
@@ -141,6 +226,15 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   u32x4 pw2 = pw;
   asm volatile("s_waitcnt vmcnt(0)" : "+v"(pw2), "+v"(lsum) : : "memory");
   const bf16x8 pf = __builtin_bit_cast(bf16x8, pw2);
+  if constexpr (kAppend) {
+    // the new v row landed in LDS row last - sbase of this wave: copy it to
+    // its cache slot (16 lanes x 16 bytes, undoing the chunk swizzle)
+    const int R = last - sbase;
+    if (R >= 32 * wave && R < 32 * wave + 32 && lane < 16) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&Vs[R * kRowBytes + 16 * (lane ^ v_swz(R))]);
+      *reinterpret_cast<u32x4 *>(a.vcw + (static_cast<int64_t>(b) * a.Tmax + last) * rstride + g * kD + 8 * lane) = v;
+    }
+  }
 
   // O^T += V^T . P^T: lane l's V^T fragment (dim 16*db + lr, slots 8*lg .. +7
   // of the wave's 32) from two transpose reads of 4 slots.
@@ -201,7 +295,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
   __shared__ float red_l[kSplitGroups];
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int g = h / a.G, hh = h % a.G;
-  const int len = a.kv_len[b];
+  const int len = a.step ? a.step[b] + 1 : a.kv_len[b];
   bf16_t *orow = a.out + (static_cast<int64_t>(b) * a.Hq + h) * kD;
   if (len < 1 || len > a.Tmax) {  // outside the contract: zero row, flag it
     if (threadIdx.x < kD) orow[threadIdx.x] = 0;
@@ -288,7 +382,50 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
   a.status = status;
   a.k1 = 2.f * mult * kLog2e / cap;
   a.k2inv = 1.f / (-2.f * cap * kLog2e);
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.S, Hkv, B), dim3(kSplitWaves * kWave), 0, st, a);
+  a.kn = a.vn = nullptr;
+  a.kcw = a.vcw = nullptr;
+  a.step = nullptr;
+  a.new_step = nullptr;
+  a.q_out = nullptr;
+  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.S, Hkv, B), dim3(kSplitWaves * kWave), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, void *kc, void *vc,
+                                const int32_t *step, int32_t *new_step, void *q_out, void *out,
+                                void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,
+                                float mult, float cap, const RopeFreqs &f, hipStream_t st) {
+  DecodeArgs a;
+  a.q = static_cast<const bf16_t *>(q);
+  a.kc = static_cast<const bf16_t *>(kc);
+  a.vc = static_cast<const bf16_t *>(vc);
+  a.kv_len = nullptr;
+  a.out = static_cast<bf16_t *>(out);
+  a.B = B;
+  a.Tmax = Tmax;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.split_keys = kSplit;
+  a.S = (Tmax + kSplit - 1) / kSplit;
+  const size_t n = static_cast<size_t>(B) * Hkv * a.S * a.G;
+  a.part_o = static_cast<float *>(ws);
+  a.part_l = a.part_o + n * kD;
+  a.status = status;
+  a.k1 = 2.f * mult * kLog2e / cap;
+  a.k2inv = 1.f / (-2.f * cap * kLog2e);
+  a.kn = static_cast<const bf16_t *>(kn);
+  a.vn = static_cast<const bf16_t *>(vn);
+  a.kcw = static_cast<bf16_t *>(kc);
+  a.vcw = static_cast<bf16_t *>(vc);
+  a.step = step;
+  a.new_step = new_step;
+  a.q_out = static_cast<bf16_t *>(q_out);
+  for (int i = 0; i < kD / 2; ++i) a.inv[i] = f.inv[i];
+  hipLaunchKernelGGL(decode_split_kernel<true>, dim3(a.S, Hkv, B), dim3(kSplitWaves * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);

@@ -242,4 +242,36 @@ int grok_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                     "attn_decode");
 }
 
+int grok_attn_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                            void *v_cache, const int32_t *step, int32_t *new_step, void *q_out,
+                            void *out, void *workspace, size_t ws_bytes, int32_t *status, int B,
+                            int Tmax, int Hq, int Hkv, int D, float attn_mult, float softcap,
+                            float rope_base, hipStream_t stream) {
+  if (B < 1 || Tmax < 1 || Hq < 1 || Hkv < 1) return fail(GROK_EINVAL, "attn_decode_append: bad shape");
+  if (Hq % Hkv) return fail(GROK_EINVAL, "attn_decode_append: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(GROK_EINVAL, "attn_decode_append: at most 16 query heads per KV head");
+  if (D != 128) return fail(GROK_EINVAL, "attn_decode_append: head size must be 128 (D=%d)", D);
+  if (bad_softmax_params(attn_mult, softcap))
+    return fail(GROK_EINVAL, "attn_decode_append: attn_mult must be finite and softcap in (0, 40]");
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return fail(GROK_EINVAL, "attn_decode_append: bad rope_base");
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !step || !out || !workspace)
+    return fail(GROK_EINVAL, "attn_decode_append: null pointer");
+  if (new_step && new_step == step) return fail(GROK_EINVAL, "attn_decode_append: new_step must not alias step");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
+                       reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
+                       reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(workspace);
+  if (al % 16) return fail(GROK_EINVAL, "attn_decode_append: misaligned pointer");
+  const size_t need = grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);
+  if (ws_bytes < need)
+    return fail(GROK_ENOMEM, "attn_decode_append: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (static_cast<int64_t>(B) * Hq > 0x7fffffff || B > 65535) return fail(GROK_EINVAL, "attn_decode_append: batch too large");
+  grok::RopeFreqs f;
+  grok::rope_build_freqs(D, rope_base, &f);
+  return hip_status(grok::launch_decode_append(q, k_new, v_new, k_cache, v_cache, step, new_step, q_out, out,
+                                               workspace, status, B, Tmax, Hq, Hkv, attn_mult, softcap, f,
+                                               stream),
+                    "attn_decode_append");
+}
+
 }  // extern "C"

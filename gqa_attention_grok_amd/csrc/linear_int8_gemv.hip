@@ -373,11 +373,9 @@ struct QkvArgs {
 };
 
 __device__ __forceinline__ void rope_pair_at(int pos, float inv, float x1, float x2, float &o1, float &o2) {
-  const float theta = __fmul_rn(static_cast<float>(pos), inv);
   float s, c;
-  sincosf(theta, &s, &c);
-  o1 = __fmaf_rn(x1, c, -__fmul_rn(x2, s));
-  o2 = __fmaf_rn(x2, c, __fmul_rn(x1, s));
+  rope_phase(pos, inv, s, c);
+  rope_rotate(x1, x2, c, s, o1, o2);
 }
 
 template <int MT, int D, bool XL, bool kNorm>

@@ -27,17 +27,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One rotated pair, with the rounding of every step pinned (no contraction)
-// so that grok_rope and the fused append produce identical bits.
+// One rotated pair (rope_rotate / rope_phase of common.h: every rounding step
+// pinned, so that grok_rope and the fused appends produce identical bits).
 __device__ __forceinline__ void rotate_pair(float x1, float x2, float c, float s, float &o1,
                                             float &o2) {
-  o1 = __fmaf_rn(x1, c, -__fmul_rn(x2, s));
-  o2 = __fmaf_rn(x2, c, __fmul_rn(x1, s));
+  rope_rotate(x1, x2, c, s, o1, o2);
 }
 
 __device__ __forceinline__ void phase_sincos(int pos, float inv, float &s, float &c) {
-  const float theta = __fmul_rn(static_cast<float>(pos), inv);
-  sincosf(theta, &s, &c);
+  rope_phase(pos, inv, s, c);
 }
 
 // Vector of V consecutive elements of type T.

@@ -6,7 +6,7 @@ owns device memory).
 
 * ``DecodeStep``   -- one decoded token per sequence (Grok-1 walkthrough, ch. 4
   "model.py close reading, part 1", §4.4): RoPE q and the new k at step[b],
-  append k/v to the cache, attend slots [0, step[b]+1).
+  append k/v to the cache, attend slots [0, step[b]+1) -- one fused call.
 * ``PrefillStep``  -- a prompt with no cache (same page, §4.3.1 and §4.5):
   RoPE q and k at positions 0..T-1, causal GQA attention.
 * ``SublayerStep`` -- the attention half of a decoder layer (ch. 6 "model.py
@@ -21,7 +21,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (grok_attn_decode, grok_attn_decode_workspace_bytes, grok_attn_prefill,
+from . import (grok_attn_decode, grok_attn_decode_append, grok_attn_decode_workspace_bytes,
+               grok_attn_prefill,
                grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
                grok_linear_int8_pack, grok_rmsnorm, grok_rope)
 
@@ -40,11 +41,17 @@ def capture(step) -> "torch.cuda.CUDAGraph":
 
 
 class DecodeStep:
+    """One decoded token per sequence: RoPE q and the new k at step[b], append
+    k/v at slot step[b], attend slots [0, step[b]+1). Fused (default): one call
+    (split kernel with the append, then the combine), q left as given;
+    unfused: the append call (rotating q in place), then the decode call."""
+
     def __init__(self, k_cache, v_cache, q, k_new, v_new, step, attn_mult, softcap=30.0,
-                 rope_base=10000.0):
+                 rope_base=10000.0, fused=True):
         self.k_cache, self.v_cache = k_cache, v_cache
         self.q, self.k_new, self.v_new, self.step = q, k_new, v_new, step
         self.attn_mult, self.softcap, self.rope_base = attn_mult, softcap, rope_base
+        self.fused = fused
         B, Tmax, Hkv, D = k_cache.shape
         Hq = q.shape[2]
         dev = q.device
@@ -54,12 +61,22 @@ class DecodeStep:
         nbytes = grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D)
         self.workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
-    def __call__(self):
-        grok_kv_append(self.k_cache, self.v_cache, self.k_new, self.v_new, self.step,
-                       q_inout=self.q, new_step=self.kv_len, status=self.status,
-                       rope_base=self.rope_base)
+    def attend(self):
+        """The attention launches alone (cache already holding the new token)."""
         grok_attn_decode(self.q, self.k_cache, self.v_cache, self.kv_len, self.out,
                          self.workspace, self.attn_mult, self.softcap, status=self.status)
+
+    def __call__(self):
+        if self.fused:
+            grok_attn_decode_append(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache,
+                                    self.step, self.out, self.workspace, self.attn_mult,
+                                    self.softcap, new_step=self.kv_len, status=self.status,
+                                    rope_base=self.rope_base)
+        else:
+            grok_kv_append(self.k_cache, self.v_cache, self.k_new, self.v_new, self.step,
+                           q_inout=self.q, new_step=self.kv_len, status=self.status,
+                           rope_base=self.rope_base)
+            self.attend()
         return self.out
 
 

@@ -244,6 +244,30 @@ GROK_API int grok_attn_decode(const void *q, const void *k_cache, const void *v_
                      int32_t *status, int B, int Tmax, int Hq, int Hkv, int D,
                      float attn_mult, float softcap, hipStream_t stream);
 
+/*
+ * One decode step of the attention core in one call ([ch4] §4.4 RoPE before
+ * the cache write, §4.5 attention): for each sequence b with p = step[b],
+ *   q_r = rope(q[b, 0], p),  k_cache[b, p] = rope(k_new[b, 0], p),
+ *   v_cache[b, p] = v_new[b, 0],  out[b, 0] = attention of q_r over slots [0, p]
+ * with the numerics (and the bits) of grok_kv_append followed by
+ * grok_attn_decode with kv_len = step + 1. q is not modified; the rotated q
+ * goes to q_out if it is not NULL. new_step[b] = p + 1 if new_step is not NULL.
+ *   q [B, 1, Hq, 128]; k_new, v_new [B, 1, Hkv, 128]; caches [B, Tmax, Hkv, 128];
+ *   step [B] int32 device (must not alias new_step); out [B, 1, Hq*128]; bf16;
+ *   workspace as for grok_attn_decode (grok_attn_decode_workspace_bytes).
+ * A sequence with step[b] outside [0, Tmax) gets no cache write, an all-zero
+ * output row, new_step[b] = step[b], and GROK_ERANGE is stored to *status.
+ * Errors: EINVAL for NULL pointers, sizes < 1, Hq % Hkv != 0, Hq/Hkv > 16,
+ * D != 128, bad attn_mult/softcap (as for prefill) or rope_base, a misaligned
+ * pointer (16 bytes), or new_step == step; ENOMEM if ws_bytes is too small.
+ */
+GROK_API int grok_attn_decode_append(const void *q, const void *k_new, const void *v_new,
+                                     void *k_cache, void *v_cache, const int32_t *step,
+                                     int32_t *new_step, void *q_out, void *out, void *workspace,
+                                     size_t ws_bytes, int32_t *status, int B, int Tmax, int Hq,
+                                     int Hkv, int D, float attn_mult, float softcap,
+                                     float rope_base, hipStream_t stream);
+
 /* Workspace bytes grok_attn_decode needs for these sizes (0 on bad sizes). */
 GROK_API size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D);
 

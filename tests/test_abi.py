@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 15, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -221,3 +221,25 @@ def test_decode_qkv_validation(lib):
     assert call(prenorm=1, B=4, d=16384) == EINVAL         # 4 x 16384 values do not fit either
     assert "at most 2 rows" in _err(lib)
     assert call(prenorm=1, B=1, eps=-1.0) == EINVAL
+
+
+def test_decode_append_validation(lib):
+    ws = lib.grok_attn_decode_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    n = ws(i(1), i(8192), i(48), i(8), i(128))
+    f = lib.grok_attn_decode_append
+    f.restype = ctypes.c_int
+
+    def call(B=1, Tmax=8192, Hq=48, Hkv=8, D=128, nbytes=n, cap=30.0, base=1e4, q=FAKE, new_step=None,
+             q_out=None):
+        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, new_step, q_out, FAKE, FAKE, ctypes.c_size_t(nbytes), None,
+                 i(B), i(Tmax), i(Hq), i(Hkv), i(D), fl(0.088), fl(cap), fl(base), None)
+    assert call(nbytes=n - 4) == ENOMEM
+    assert call(D=64) == EINVAL
+    assert call(Hq=44) == EINVAL
+    assert call(Hq=136) == EINVAL          # 17 query heads per KV head
+    assert call(cap=45.0) == EINVAL
+    assert call(base=-1.0) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(new_step=FAKE) == EINVAL   # aliases step
+    assert call(q_out=ctypes.c_void_p(0x10008)) == EINVAL

@@ -400,6 +400,58 @@ def test_decode(G, Hq, Hkv, lens, Tmax):
     assert U.rel_l2(U.host(out), ref) < 1e-2
 
 
+@pytest.mark.parametrize("Hq,Hkv,lens,Tmax", [
+    (48, 8, [300, 1, 129, 128], 300),   # a full cache, a one-slot sequence, split boundaries
+    (6, 3, [200, 77, 1], 200),
+    (16, 1, [1000], 1024),              # 16 query heads on one KV head
+])
+def test_decode_append_matches_unfused_calls(G, Hq, Hkv, lens, Tmax):
+    """RoPE + append inside the split kernel give the bits of the append call
+    followed by the decode call: output, both caches, rotated q, new_step."""
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    B, D = len(lens), 128
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=Hq * 7 + Tmax, lengths=lens)
+    mult = 1 / math.sqrt(D)
+    res = []
+    for fused in (False, True):
+        kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+        st = pipe.DecodeStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                             U.dev(p["step"]), mult, fused=fused)
+        out = st()
+        qo = torch.empty_like(st.q)
+        if fused:  # the rotated q, as the unfused append leaves it in q
+            grok.grok_attn_decode_append(st.q, st.k_new, st.v_new, kc, vc, st.step, out, st.workspace, mult,
+                                         new_step=st.kv_len, q_out=qo, status=st.status)
+        else:
+            qo.copy_(st.q)
+        torch.cuda.synchronize()
+        assert st.status.item() == 0
+        res.append((U.bits(out), U.bits(kc), U.bits(vc), U.bits(qo), st.kv_len.cpu().numpy()))
+    for a, b_ in zip(*res):
+        np.testing.assert_array_equal(a, b_)
+    np.testing.assert_array_equal(res[1][4], lens)
+
+
+def test_decode_append_bad_step(G):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    B, Hq, Hkv, D, Tmax = 3, 12, 2, 128, 64
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=9, lengths=[10, 10, 10])
+    steps = np.array([5, Tmax, -1], np.int32)
+    kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    st = pipe.DecodeStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                         U.dev(steps), 0.1)
+    out = U.host(st()).reshape(B, -1)
+    torch.cuda.synchronize()
+    assert st.status.item() == -34
+    np.testing.assert_array_equal(st.kv_len.cpu().numpy(), [6, Tmax, -1])
+    assert np.all(out[1:] == 0) and np.any(out[0] != 0)
+    kcb = U.bits(kc)
+    np.testing.assert_array_equal(kcb[1:], p["k_cache"][1:])   # nothing written for the bad ones
+    np.testing.assert_array_equal(kcb[0, :5], p["k_cache"][0, :5])
+
+
 def test_decode_bad_lengths_give_zero_rows_and_status(G):
     grok, U, torch = G
     B, Tmax, Hq, Hkv, D = 3, 256, 48, 8, 128
