@@ -38,6 +38,7 @@ __all__ = [
     "make_decode_inputs",
     "make_sublayer_inputs",
     "make_decode_sublayer_inputs",
+    "make_chunk_inputs",
     "make_workload",
 ]
 
@@ -79,7 +80,7 @@ def int8_uniform(g: np.random.Generator, shape) -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "sublayer" | "decode_sublayer"
+    kind: str  # "prefill" | "decode" | "sublayer" | "decode_sublayer" | "chunk"
     seed: int
     dtype: str  # "f32" | "bf16"
     B: int
@@ -131,6 +132,11 @@ WORKLOADS = {
     "decode_sublayer_b32_t8192": Workload(
         name="decode_sublayer_b32_t8192", kind="decode_sublayer", seed=1007, dtype="bf16",
         B=32, Hq=48, Hkv=8, D=128, Tmax=8192, d_model=6144, ragged=True),
+    # Chunked prefill: 512 new tokens per sequence after a cached prefix of
+    # uniform length in [0, 7680] (4 sequences).
+    "prefill_chunk_b4_t512": Workload(
+        name="prefill_chunk_b4_t512", kind="chunk", seed=1008, dtype="bf16",
+        B=4, T=512, Hq=48, Hkv=8, D=128, Tmax=8192),
 }
 
 
@@ -212,6 +218,23 @@ def make_decode_sublayer_inputs(B, d_model, Hq, Hkv, D, Tmax, seed, lengths=None
     return out
 
 
+def make_chunk_inputs(B, T, Hq, Hkv, D, Tmax, seed, offsets=None):
+    """A cache [B,Tmax,Hkv,D] (every slot finite N(0,1); slots below the offset
+    are the cached prefix, used as already rotated), T new q/k/v rows per
+    sequence, and step = offset = the cached length, uniform in [0, Tmax-T]."""
+    g = rng(seed)
+    k_cache = normal_bf16(g, (B, Tmax, Hkv, D))
+    v_cache = normal_bf16(g, (B, Tmax, Hkv, D))
+    q = normal_bf16(g, (B, T, Hq, D))
+    k_new = normal_bf16(g, (B, T, Hkv, D))
+    v_new = normal_bf16(g, (B, T, Hkv, D))
+    if offsets is None:
+        offsets = g.integers(0, Tmax - T + 1, size=B)
+    step = np.asarray(offsets, dtype=np.int32)
+    return {"k_cache": k_cache, "v_cache": v_cache, "q": q, "k_new": k_new, "v_new": v_new,
+            "step": step}
+
+
 def make_workload(name: str) -> dict:
     """All inputs of one named workload at its full size."""
     w = WORKLOADS[name]
@@ -219,6 +242,8 @@ def make_workload(name: str) -> dict:
         return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.seed, w.dtype)
     if w.kind == "decode":
         return make_decode_inputs(w.B, w.Hq, w.Hkv, w.D, w.Tmax, w.seed, ragged=w.ragged)
+    if w.kind == "chunk":
+        return make_chunk_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.Tmax, w.seed)
     if w.kind == "decode_sublayer":
         return make_decode_sublayer_inputs(w.B, w.d_model, w.Hq, w.Hkv, w.D, w.Tmax, w.seed,
                                            ragged=w.ragged)

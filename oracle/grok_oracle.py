@@ -56,6 +56,7 @@ __all__ = [
     "decode_step",
     "sublayer",
     "decode_sublayer",
+    "chunk_prefill",
     "kv_cache_bytes",
 ]
 
@@ -340,6 +341,28 @@ def decode_sublayer(x, k_cache, v_cache, step, wq, sq, wk, sk, wv, sv, wo, so, H
     a, kc, vc, new_step = decode_step(k_cache, v_cache, q, k, v, step, mult, cap, base, io)
     o = linear_int8(a, wo, so, out=io)
     return rmsnorm(o, None, eps, residual=x, out=io), kc, vc, new_step
+
+
+def chunk_prefill(k_cache, v_cache, q, k_new, v_new, step, mult, cap=30.0, base=10000.0,
+                  io="bf16"):
+    """A chunk of T new tokens per sequence into a non-empty memory ([ch4] §4.4
+    RoPE before the cache write; [ch6] §6.6.1 per-sequence step).
+
+    The pages' mask shapes do not cover T > 1 after a non-empty memory; the
+    causal rule is taken on absolute positions: token t of sequence b sits at
+    position p = step[b] + t, is rotated there, written to slot p, and attends
+    slots [0, p]. Inputs are float64 values already in the I/O dtype. Returns
+    (out [B, T, Hq*D], k_cache', v_cache', new_step = step + T).
+    """
+    B, T = q.shape[:2]
+    pos = np.asarray(step, dtype=np.int64).reshape(B, 1) + np.arange(T)
+    qr = rope(q, pos, base, out=io)
+    kr = rope(k_new, pos, base, out=io)
+    kc, vc, new_step = kv_append(k_cache, v_cache, kr, np.asarray(v_new, np.float64), step)
+    Tmax = kc.shape[1]
+    mask = attention_mask(pos, Tmax, kv_len=new_step)
+    o = attention(qr, kc, vc, mask, mult, cap, out=io)
+    return o, kc, vc, new_step
 
 
 def kv_cache_bytes(num_layers, batch, seq_len, num_kv_heads, head_size, elem_bytes=2):

@@ -464,3 +464,37 @@ def test_decode_sublayer_zero_output_projection_is_identity():
                                      p["wk"], p["sk"], p["wv"], p["sv"], np.zeros_like(p["wo"]),
                                      p["so"], Hq, Hkv, D, 0.35)
     np.testing.assert_array_equal(y, x)
+
+
+def test_chunk_prefill_at_zero_is_prefill_and_chunks_compose():
+    """A chunk into an empty memory is the cache-free causal prefill, and two
+    chunks in a row give the rows of one prefill over the whole prompt."""
+    g = np.random.default_rng(51)
+    B, T1, T2, Hq, Hkv, D, Tmax = 2, 5, 4, 6, 2, 16, 12
+    T = T1 + T2
+    q, k, v = (g.standard_normal((B, T, H, D)) for H in (Hq, Hkv, Hkv))
+    pos = np.broadcast_to(np.arange(T), (B, T))
+    full = orc.attention(orc.rope(q, pos), orc.rope(k, pos), v, orc.attention_mask(pos, T), 0.3)
+    kc = g.standard_normal((B, Tmax, Hkv, D)) * 5
+    vc = g.standard_normal((B, Tmax, Hkv, D)) * 5
+    o1, kc1, vc1, ns1 = orc.chunk_prefill(kc, vc, q[:, :T1], k[:, :T1], v[:, :T1], np.zeros(B, np.int32),
+                                          0.3, io=None)
+    np.testing.assert_allclose(o1, full[:, :T1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(ns1, T1)
+    o2, kc2, vc2, ns2 = orc.chunk_prefill(kc1, vc1, q[:, T1:], k[:, T1:], v[:, T1:], ns1, 0.3, io=None)
+    np.testing.assert_allclose(o2, full[:, T1:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(ns2, T)
+    np.testing.assert_array_equal(kc2[:, T:], kc[:, T:])  # slots past the prompt untouched
+
+
+def test_chunk_prefill_of_one_token_is_a_decode_step():
+    g = np.random.default_rng(52)
+    B, Hq, Hkv, D, Tmax = 3, 4, 2, 8, 10
+    q, k, v = (g.standard_normal((B, 1, H, D)) for H in (Hq, Hkv, Hkv))
+    kc = g.standard_normal((B, Tmax, Hkv, D))
+    vc = g.standard_normal((B, Tmax, Hkv, D))
+    step = np.array([0, 4, 9], np.int32)
+    a = orc.chunk_prefill(kc, vc, q, k, v, step, 0.2, io=None)
+    b = orc.decode_step(kc, vc, q, k, v, step, 0.2, io=None)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-14)
