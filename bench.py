@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default="", help="comma list of prefill,decode_b1,decode_ragged,sublayer,"
-                    "decode_sublayer_b1,decode_sublayer_b32 (default: all)")
+                    "decode_sublayer_b1,decode_sublayer_b32,chunk (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (HBM counter calibration)")
@@ -222,6 +222,24 @@ def bench_decode_sublayer(torch, grok, pipe, U, gi, name, steps, warmup, replica
     }
 
 
+def bench_chunk(torch, grok, pipe, U, gi, steps, warmup, replicas=2):
+    """One step = RoPE + append of a 512-token chunk per sequence, then its
+    causal attention over the cached prefix and itself."""
+    w = gi.WORKLOADS["prefill_chunk_b4_t512"]
+    p = gi.make_workload(w.name)
+    q, kn, vn, stp = U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]), U.dev(p["step"])
+    steps_obj = [pipe.ChunkStep(U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"]), q, kn, vn, stp, w.attn_mult,
+                                w.softcap) for _ in range(replicas)]
+    offs = p["step"].astype(np.int64)
+    del p
+    flop = int(sum(4 * w.D * w.Hq * (w.T * (o + 1) + w.T * (w.T - 1) // 2) for o in offs))
+    sec = time_steps(torch, pipe, steps_obj, steps, warmup)
+    kern_ms = time_kernel(torch, lambda i: steps_obj[i % replicas].attend(), max(steps, 2 * replicas))
+    return {"workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12, "unit": "TFLOP/s",
+            "flop_per_step": flop, "offsets": [int(o) for o in offs], "kernel": "prefill_mfma_kernel (offset)",
+            "kernel_ms": kern_ms, "kernel_tflops": flop / (kern_ms * 1e-3) / 1e12}
+
+
 def cpu_baseline(gi, orc):
     """The fp64 oracle on a bounded sample of the 8k prefill: all 48 heads of
     256 query rows spread over the sequence (RoPE of the sampled q rows and of
@@ -268,7 +286,7 @@ def main():
     import gpu_util as U
 
     only = set(args.only.split(",")) if args.only else {"prefill", "decode_b1", "decode_ragged", "sublayer",
-                                                        "decode_sublayer_b1", "decode_sublayer_b32"}
+                                                        "decode_sublayer_b1", "decode_sublayer_b32", "chunk"}
     res = {}
     if args.copy_calibration:
         # a plain copy of known size: reads and writes exactly 256 MiB
@@ -303,6 +321,9 @@ def main():
             print(f"# {key} done: {res[key]['value']:.1f} GB/s, {res[key]['ms_per_step'] * 1e3:.1f} us/step",
                   file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+    if "chunk" in only:
+        res["chunk"] = bench_chunk(torch, grok, pipe, U, gi, args.steps, args.warmup)
+        print(f"# chunk done: {res['chunk']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     head = res.get("prefill") or next(iter(res.values()))
     line = {

@@ -22,7 +22,7 @@ __all__ = [
     "grok_abi_version", "grok_status_string", "grok_last_error",
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
     "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
-    "grok_attn_prefill", "grok_attn_decode", "grok_attn_decode_append",
+    "grok_attn_prefill", "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
     "grok_attn_decode_workspace_bytes",
 ]
 
@@ -54,6 +54,7 @@ _PROTOS = {
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
     "grok_attn_decode": (_i, [_p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i, _f, _f, _p]),
     "grok_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "grok_attn_prefill_chunk": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _p]),
     "grok_attn_decode_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i,
                                      _f, _f, _f, _p]),
 }
@@ -306,4 +307,21 @@ def grok_attn_decode_append(q, k_new, v_new, k_cache, v_cache, step, out, worksp
                                        _ptr(step), _ptr(new_step), _ptr(q_out), _ptr(out), _ptr(workspace),
                                        ws_bytes, _ptr(status), B, Tmax, Hq, Hkv, D, attn_mult, softcap,
                                        rope_base, _stream(q)), "grok_attn_decode_append")
+    return out
+
+
+def grok_attn_prefill_chunk(q, k_cache, v_cache, offset, out, attn_mult, softcap=30.0, status=None):
+    """Chunk of T tokens per sequence at positions offset[b] + t, attending cache
+    slots [0, offset[b] + t]; q [B,T,Hq,D] rotated, out [B,T,Hq*D]."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(offset, "offset", torch.int32, 1)
+    _need(out, "out", torch.bfloat16)
+    _need(status, "status", torch.int32)
+    B, T, Hq, D = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(lib.grok_attn_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(offset), _ptr(out),
+                                       _ptr(status), B, T, Tmax, Hq, Hkv, D, attn_mult, softcap, _stream(q)),
+           "grok_attn_prefill_chunk")
     return out

@@ -96,7 +96,8 @@ hipError_t launch_prefill_generic(const void *q, const void *k, const void *v, i
                                   hipStream_t s);
 hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int64_t kv_rows,
                                const uint8_t *key_valid, void *out, int B, int T, int Hq,
-                               int Hkv, float mult, float cap, hipStream_t s);
+                               int Hkv, float mult, float cap, hipStream_t s,
+                               const int32_t *offset = nullptr, int32_t *status = nullptr);
 bool prefill_mfma_supported(int64_t kv_rows, int Hq, int Hkv, int D, int dtype);
 hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int32_t *kv_len,
                          void *out, void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,

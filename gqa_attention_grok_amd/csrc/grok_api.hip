@@ -274,4 +274,24 @@ int grok_attn_decode_append(const void *q, const void *k_new, const void *v_new,
                     "attn_decode_append");
 }
 
+int grok_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *offset, void *out, int32_t *status, int B, int T, int Tmax,
+                            int Hq, int Hkv, int D, float attn_mult, float softcap, hipStream_t stream) {
+  if (B < 1 || T < 1 || Tmax < 1 || Hq < 1 || Hkv < 1) return fail(GROK_EINVAL, "attn_prefill_chunk: bad shape");
+  if (T > Tmax) return fail(GROK_EINVAL, "attn_prefill_chunk: T=%d exceeds Tmax=%d", T, Tmax);
+  if (Hq % Hkv) return fail(GROK_EINVAL, "attn_prefill_chunk: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (D != 128) return fail(GROK_EINVAL, "attn_prefill_chunk: head size must be 128 (D=%d)", D);
+  if (bad_softmax_params(attn_mult, softcap))
+    return fail(GROK_EINVAL, "attn_prefill_chunk: attn_mult must be finite and softcap in (0, 40]");
+  if (!q || !k_cache || !v_cache || !offset || !out) return fail(GROK_EINVAL, "attn_prefill_chunk: null pointer");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out);
+  if (al % 16) return fail(GROK_EINVAL, "attn_prefill_chunk: misaligned pointer");
+  if (!grok::prefill_mfma_supported(Tmax, Hq, Hkv, D, GROK_BF16))
+    return fail(GROK_EINVAL, "attn_prefill_chunk: unsupported sizes");
+  return hip_status(grok::launch_prefill_mfma(q, k_cache, v_cache, Tmax, nullptr, out, B, T, Hq, Hkv, attn_mult,
+                                              softcap, stream, offset, status),
+                    "attn_prefill_chunk");
+}
+
 }  // extern "C"

@@ -58,13 +58,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct PrefillArgs {
   const bf16_t *q, *k, *v;
   const uint8_t *key_valid;
+  const int32_t *offset;  // kOffset: position of each sequence's first query row
+  int32_t *status;
   bf16_t *out;
   int64_t kv_rows;
   int B, T, Hq, Hkv, G, Gc, npb, nhc, nqt;
   float k1, k2inv;  // exp2 scale inside the softcap; 1 / (outer exp2 scale)
 };
 
-template <bool kHasValid>
+// kOffset: the T query rows of sequence b sit at positions offset[b] + t (a
+// chunk after a cached prefix) and attend keys [0, offset[b] + t] of K/V
+// read in place from the cache (kv_rows = its capacity); without it the
+// offset is 0 and the code is the plain causal prefill.
+template <bool kHasValid, bool kOffset>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][kTileBytes];
@@ -86,11 +92,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   const int qt = a.nqt - 1 - (id % a.nqt);
   const int b = id / a.nqt;
   const int span = 16 * a.npb;
-  const int p0 = qt * span;
+  // o: position of row 0; klen: keys [0, klen) exist (prefix + this chunk)
+  const int o = kOffset ? a.offset[b] : 0;
+  const int klen = o + a.T;
+  const int p0 = qt * span;  // first row of the workgroup (row index)
   const int kend = min(a.T, p0 + span);
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int ntiles = (o + kend + kBN - 1) / kBN;
 
-  // This wave's row blocks.
+  // This wave's row blocks; pos[] are positions (row index + o).
   int head[kRB], pos[kRB];
   int wmin = 1 << 30, wmax = -1;
 #pragma unroll
@@ -98,11 +107,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     const int r = wave * kRB + i;
     head[i] = g * a.G + hc * a.Gc + (r % a.Gc);
     const int pb = r / a.Gc;
-    pos[i] = p0 + 16 * pb + lr;
-    wmin = min(wmin, p0 + 16 * pb);
-    wmax = max(wmax, p0 + 16 * pb + 15);
+    pos[i] = o + p0 + 16 * pb + lr;
+    wmin = min(wmin, o + p0 + 16 * pb);
+    wmax = max(wmax, o + p0 + 16 * pb + 15);
   }
-  wmax = min(wmax, a.T - 1);
+  wmax = min(wmax, klen - 1);
+  if constexpr (kOffset) {
+    if (o < 0 || static_cast<int64_t>(klen) > a.kv_rows) {  // outside the cache: zero rows, flag it
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        const int row = pos[i] - o;
+        if (row >= a.T) continue;
+        bf16_t *orow = a.out + ((static_cast<int64_t>(b) * a.T + row) * a.Hq + head[i]) * kD;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *reinterpret_cast<u32x2 *>(orow + 16 * db + 4 * lg) = u32x2{0u, 0u};
+      }
+      if (tid == 0 && a.status) *a.status = GROK_ERANGE;
+      return;
+    }
+  }
 
   // Tile loads, HBM -> LDS. Each wave moves 4 KB of K and 4 KB of V per tile:
   // instruction j (0..3) fills 1 KB = LDS rows 16*wave + 4*j .. +3, lane L
@@ -111,8 +134,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   // swizzle (R % 8 = 4*(j%2) + L/16) alternates with the parity of j. Row R of
   // the V tile holds key R, with swizzle 2*(L/16) for every j. So one per-lane
   // byte offset per K parity and one for V, plus a wave-uniform base, address
-  // all eight loads. Keys at or past T (ragged last tile) read row T-1 instead:
-  // they are masked out below.
+  // all eight loads. Keys at or past klen (ragged last tile) read row klen-1
+  // instead: they are masked out below.
   const bf16_t *kbase = a.k + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
   const bf16_t *vbase = a.v + (static_cast<int64_t>(b) * a.kv_rows * a.Hkv + g) * kD;
   const int64_t rstride = static_cast<int64_t>(a.Hkv) * kD;
@@ -122,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   const uint32_t koff = key_l * rs2;
   const uint32_t voff = lrow * rs2;
   auto issue_tile = [&](int key0, int buf) {
-    if (key0 + kBN <= a.T) {
+    if (key0 + kBN <= klen) {
       const char *kt = reinterpret_cast<const char *>(kbase) + static_cast<int64_t>(key0) * rs2;
       const char *vt = reinterpret_cast<const char *>(vbase) + static_cast<int64_t>(key0 + 16 * wave) * rs2;
 #pragma unroll
@@ -138,12 +161,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int R = 16 * wave + 4 * j + lrow;
-      const int kj = min(key0 + k_row_key(R), a.T - 1);
+      const int kj = min(key0 + k_row_key(R), klen - 1);
       const int kc = lchunk ^ (R & 15);
       __builtin_amdgcn_global_load_lds(kbase + kj * rstride + 8 * kc,
                                        (lds_void *)(&Ks[buf][(16 * wave + 4 * j) * kRowBytes]),
                                        16, 0, 0);
-      const int vj = min(key0 + R, a.T - 1);
+      const int vj = min(key0 + R, klen - 1);
       const int vc = lchunk ^ v_swz(R);
       __builtin_amdgcn_global_load_lds(vbase + vj * rstride + 8 * vc,
                                        (lds_void *)(&Vs[buf][(16 * wave + 4 * j) * kRowBytes]),
@@ -169,8 +192,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   bf16x8 qf[kRB][4];
 #pragma unroll
   for (int i = 0; i < kRB; ++i) {
-    const bool ok = pos[i] < a.T;
-    const bf16_t *qp = a.q + ((static_cast<int64_t>(b) * a.T + (ok ? pos[i] : 0)) * a.Hq + head[i]) * kD;
+    const int row = pos[i] - o;
+    const bool ok = row < a.T;
+    const bf16_t *qp = a.q + ((static_cast<int64_t>(b) * a.T + (ok ? row : 0)) * a.Hq + head[i]) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 w = ok ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * lg) : u32x4{0, 0, 0, 0};
@@ -293,8 +317,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     __syncthreads();
   };
 
-  // Tiles [0, tfull) end below the workgroup's first query row p0.
-  const int tfull = kHasValid ? 0 : p0 / kBN;
+  // Tiles [0, tfull) end below the workgroup's first query position o + p0.
+  const int tfull = kHasValid ? 0 : (o + p0) / kBN;
   int t = 0;
   for (; t < tfull; ++t) tile(t, std::false_type{});
   for (; t < ntiles; ++t) tile(t, std::true_type{});
@@ -305,8 +329,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     float l = lsum[i];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
-    if (pos[i] >= a.T) continue;
-    bf16_t *orow = a.out + ((static_cast<int64_t>(b) * a.T + pos[i]) * a.Hq + head[i]) * kD;
+    const int row = pos[i] - o;
+    if (row >= a.T) continue;
+    bf16_t *orow = a.out + ((static_cast<int64_t>(b) * a.T + row) * a.Hq + head[i]) * kD;
     if (kHasValid && l == 0.f) {
       // No valid key for this row: equal weights on all T value rows.
       f32x4 acc[8];
@@ -356,8 +381,11 @@ bool prefill_mfma_supported(int64_t kv_rows, int Hq, int Hkv, int D, int dtype) 
 
 hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int64_t kv_rows,
                                const uint8_t *key_valid, void *out, int B, int T, int Hq,
-                               int Hkv, float mult, float cap, hipStream_t s) {
+                               int Hkv, float mult, float cap, hipStream_t s,
+                               const int32_t *offset, int32_t *status) {
   PrefillArgs a;
+  a.offset = offset;
+  a.status = status;
   a.q = static_cast<const bf16_t *>(q);
   a.k = static_cast<const bf16_t *>(k);
   a.v = static_cast<const bf16_t *>(v);
@@ -377,11 +405,15 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int6
   a.k2inv = 1.f / (-2.f * cap * kLog2e);
   const int64_t nblk = static_cast<int64_t>(B) * Hkv * a.nhc * a.nqt;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (key_valid)
-    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+  if (offset && key_valid) return hipErrorInvalidValue;  // validated by the caller
+  if (offset)
+    hipLaunchKernelGGL((prefill_mfma_kernel<false, true>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+                       s, a);
+  else if (key_valid)
+    hipLaunchKernelGGL((prefill_mfma_kernel<true, false>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
                        s, a);
   else
-    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((prefill_mfma_kernel<false, false>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
                        s, a);
   return hipGetLastError();
 }

@@ -12,6 +12,9 @@ owns device memory).
 * ``SublayerStep`` -- the attention half of a decoder layer (ch. 6 "model.py
   close reading, part 3", §6.3.1): h = x + norm(Wo . attn(rope(Wq n),
   rope(Wk n), Wv n)) with n = norm(x).
+* ``ChunkStep``    -- a chunk of T new tokens per sequence after a cached
+  prefix (ch. 4 §4.4, ch. 6 §6.6.1): RoPE q and k at step[b] + t, append k/v,
+  causal attention on absolute positions over the cache.
 * ``DecodeSublayerStep`` -- the same sub-layer for one new token per sequence
   against the KV memory (ch. 4 §4.4, ch. 6 §6.6): the projections are few-row
   products that stream the int8 weights once, and the attention is the
@@ -22,7 +25,7 @@ from __future__ import annotations
 import torch
 
 from . import (grok_attn_decode, grok_attn_decode_append, grok_attn_decode_workspace_bytes,
-               grok_attn_prefill,
+               grok_attn_prefill, grok_attn_prefill_chunk,
                grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
                grok_linear_int8_pack, grok_rmsnorm, grok_rope)
 
@@ -98,6 +101,35 @@ class PrefillStep:
 
     def __call__(self):
         self.rope()
+        return self.attend()
+
+
+class ChunkStep:
+    """Chunked prefill: append (RoPE q in place and k into the cache at
+    step[b] + t), then the chunk's attention over cache slots [0, step[b] + t]."""
+
+    def __init__(self, k_cache, v_cache, q, k_new, v_new, step, attn_mult, softcap=30.0,
+                 rope_base=10000.0):
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.q, self.k_new, self.v_new, self.step = q, k_new, v_new, step
+        self.attn_mult, self.softcap, self.rope_base = attn_mult, softcap, rope_base
+        B, T, Hq, D = q.shape
+        dev = q.device
+        self.out = torch.empty((B, T, Hq * D), dtype=torch.bfloat16, device=dev)
+        self.new_step = torch.empty_like(step)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def append(self):
+        grok_kv_append(self.k_cache, self.v_cache, self.k_new, self.v_new, self.step,
+                       q_inout=self.q, new_step=self.new_step, status=self.status,
+                       rope_base=self.rope_base)
+
+    def attend(self):
+        return grok_attn_prefill_chunk(self.q, self.k_cache, self.v_cache, self.step, self.out,
+                                       self.attn_mult, self.softcap, status=self.status)
+
+    def __call__(self):
+        self.append()
         return self.attend()
 
 

@@ -222,6 +222,30 @@ GROK_API int grok_attn_prefill(const void *q, const void *k, const void *v, int6
                       int D, float attn_mult, float softcap, int dtype, hipStream_t stream);
 
 /*
+ * Causal grouped-query attention of a chunk of T new tokens per sequence
+ * after a cached prefix (continuation / chunked prefill; [ch4] §4.4, §4.5,
+ * [ch6] §6.6.1). The pages' mask shapes do not cover this case; the causal
+ * rule is applied on absolute positions: query row t of sequence b sits at
+ * position p = offset[b] + t and attends cache slots [0, p]:
+ *   out[b,t,h*D:(h+1)*D] = sum_{j <= p} softmax_j(softcap * tanh(attn_mult *
+ *                           <q[b,t,h], k_cache[b,j,g]> / softcap)) * v_cache[b,j,g]
+ *   q      [B, T, Hq, 128] bf16, already rotated at its positions;
+ *   caches [B, Tmax, Hkv, 128] bf16 holding slots [0, offset[b] + T) (the
+ *          chunk's own keys and values included, e.g. written by
+ *          grok_kv_append with step = offset); only those slots are read;
+ *   offset [B] int32 device; out [B, T, Hq*128] bf16.
+ * A sequence with offset[b] < 0 or offset[b] + T > Tmax gets all-zero output
+ * rows and GROK_ERANGE is stored to *status (if not NULL).
+ * Errors: EINVAL for NULL pointers, sizes < 1, T > Tmax, Hq % Hkv != 0,
+ * D != 128, bad attn_mult/softcap (as for prefill), or a pointer not 16-byte
+ * aligned.
+ */
+GROK_API int grok_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *offset, void *out, int32_t *status, int B,
+                                     int T, int Tmax, int Hq, int Hkv, int D, float attn_mult,
+                                     float softcap, hipStream_t stream);
+
+/*
  * Single-token decode attention against a KV cache ([ch4] §4.4, §4.5; the
  * causal mask of one query is all-ones and the memory mask keeps slots
  * j < kv_len[b]):

@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 16, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -243,3 +243,15 @@ def test_decode_append_validation(lib):
     assert call(q=None) == EINVAL
     assert call(new_step=FAKE) == EINVAL   # aliases step
     assert call(q_out=ctypes.c_void_p(0x10008)) == EINVAL
+
+
+def test_prefill_chunk_validation(lib):
+    def call(B=1, T=512, Tmax=8192, Hq=48, Hkv=8, D=128, cap=30.0, q=FAKE, off=FAKE):
+        return _c(lib, "grok_attn_prefill_chunk", q, FAKE, FAKE, off, FAKE, None, i(B), i(T), i(Tmax), i(Hq),
+                  i(Hkv), i(D), fl(0.088), fl(cap), None)
+    assert call(T=9000) == EINVAL      # more rows than the cache holds
+    assert call(D=64) == EINVAL
+    assert call(Hq=44) == EINVAL
+    assert call(cap=0.0) == EINVAL
+    assert call(off=None) == EINVAL
+    assert call(q=ctypes.c_void_p(0x10004)) == EINVAL

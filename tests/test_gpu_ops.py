@@ -324,6 +324,54 @@ def test_prefill_mfma(G, B, T, Hq, Hkv, scale):
     _prefill_case(G, B, T, Hq, Hkv, 128, "bf16", scale / math.sqrt(128), seed=B * T + Hq)
 
 
+@pytest.mark.parametrize("B,T,Hq,Hkv,Tmax,offsets", [
+    (3, 37, 48, 8, 300, [0, 63, 263]),   # empty prefix, unaligned prefix, chunk ending at Tmax
+    (2, 100, 6, 1, 256, [128, 5]),
+    (1, 1, 16, 2, 64, [40]),             # one token: a decode step
+    (2, 130, 12, 2, 400, [64, 270]),     # several query tiles
+])
+def test_prefill_chunk(G, B, T, Hq, Hkv, Tmax, offsets):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    D, mult = 128, 1 / math.sqrt(128)
+    p = gi.make_chunk_inputs(B, T, Hq, Hkv, D, Tmax, seed=B * T + Tmax, offsets=offsets)
+    kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    st = pipe.ChunkStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                        U.dev(p["step"]), mult)
+    out = U.host(st())
+    torch.cuda.synchronize()
+    assert st.status.item() == 0
+    np.testing.assert_array_equal(st.new_step.cpu().numpy(), np.asarray(offsets) + T)
+    to64 = orc.bf16_bits_to_f64
+    ref, kc2, vc2, _ = orc.chunk_prefill(to64(p["k_cache"]), to64(p["v_cache"]), to64(p["q"]), to64(p["k_new"]),
+                                         to64(p["v_new"]), p["step"], mult)
+    U.assert_bf16_close(out, ref, f"chunk B={B} T={T} offsets={offsets}")
+    # the cache: v slots bit copies, k slots rotated, nothing else touched
+    kcb, vcb = U.bits(kc), U.bits(vc)
+    for b, o in enumerate(offsets):
+        np.testing.assert_array_equal(vcb[b, o:o + T], p["v_new"][b])
+        U.assert_bf16_close(to64(kcb[b, o:o + T]), kc2[b, o:o + T], "chunk k slots")
+        np.testing.assert_array_equal(kcb[b, :o], p["k_cache"][b, :o])
+        np.testing.assert_array_equal(kcb[b, o + T:], p["k_cache"][b, o + T:])
+
+
+def test_prefill_chunk_at_offset_zero_is_the_prefill_bit_for_bit_and_bad_offsets(G):
+    grok, U, torch = G
+    B, T, Hq, Hkv, D, Tmax = 2, 150, 48, 8, 128, 256
+    p = gi.make_chunk_inputs(B, T, Hq, Hkv, D, Tmax, seed=77, offsets=[0, 0])
+    q, kc, vc = U.dev_bf16(p["q"]), U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    a = torch.empty((B, T, Hq * D), dtype=torch.bfloat16, device="cuda")
+    b_ = torch.empty_like(a)
+    grok.grok_attn_prefill_chunk(q, kc, vc, U.dev(p["step"]), a, 0.2)
+    grok.grok_attn_prefill(q, kc, vc, b_, 0.2)          # K/V read in place, row stride Tmax
+    np.testing.assert_array_equal(U.bits(a), U.bits(b_))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grok.grok_attn_prefill_chunk(q, kc, vc, U.dev(np.array([-1, Tmax - T + 1], np.int32)), a, 0.2, status=status)
+    torch.cuda.synchronize()
+    assert status.item() == -34
+    assert not np.any(U.host(a))
+
+
 def test_prefill_mfma_padding_and_fully_masked_rows(G):
     B, T = 2, 77
     pad = np.ones((B, T), np.uint8)

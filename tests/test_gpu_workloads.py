@@ -200,3 +200,32 @@ def test_decode_sublayer_workloads(G, name, seqs):
                                         magnitude=np.maximum(np.abs(ref), np.abs(nt))))
         print(f"{name} b={b}: rel L2 {U.rel_l2(y[sl], ref):.2e}", flush=True)
     print(f"{name}: max abs err {max(errs):.2e}")
+
+
+def test_prefill_chunk_b4_t512_sampled(G):
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS["prefill_chunk_b4_t512"]
+    p = gi.make_workload(w.name)
+    kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    st = pipe.ChunkStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                        U.dev(p["step"]), w.attn_mult, w.softcap)
+    out = U.host(st())
+    torch.cuda.synchronize()
+    assert st.status.item() == 0
+    B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+    to64 = orc.bf16_bits_to_f64
+    g = gi.rng(4343)
+    errs = []
+    for b in range(B):
+        o = int(p["step"][b])
+        pos = (o + np.arange(T))[None]
+        qr = orc.rope(to64(p["q"][b:b + 1]), pos, out="bf16")
+        kr = orc.rope(to64(p["k_new"][b:b + 1]), pos, out="bf16")
+        k64 = np.concatenate([to64(p["k_cache"][b:b + 1, :o]), kr], axis=1)
+        v64 = np.concatenate([to64(p["v_cache"][b:b + 1, :o]), to64(p["v_new"][b:b + 1])], axis=1)
+        for t in [0, T - 1] + list(g.integers(0, T, 2)):
+            mask_row = np.arange(o + T) <= o + t
+            ref = np.concatenate([orc.attention_rows(qr, k64, v64, 0, t, h, mask_row, w.attn_mult, w.softcap)
+                                  for h in range(Hq)])
+            errs.append(U.assert_bf16_close(out[b, t], ref, f"chunk b={b} (offset {o}) t={t}"))
+    print(f"chunk sampled rows, max abs err {max(errs):.2e}")
