@@ -39,6 +39,7 @@ __all__ = [
     "make_sublayer_inputs",
     "make_decode_sublayer_inputs",
     "make_chunk_inputs",
+    "make_moe_inputs",
     "make_workload",
 ]
 
@@ -80,7 +81,7 @@ def int8_uniform(g: np.random.Generator, shape) -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "prefill" | "decode" | "sublayer" | "decode_sublayer" | "chunk"
+    kind: str  # "prefill" | "decode" | "sublayer" | "decode_sublayer" | "chunk" | "moe"
     seed: int
     dtype: str  # "f32" | "bf16"
     B: int
@@ -94,6 +95,9 @@ class Workload:
     softcap: float = 30.0
     rope_base: float = 10000.0
     eps: float = 1e-5
+    d_ffn: int = 0       # MoE expert width
+    n_experts: int = 0   # MoE
+    top_k: int = 0       # MoE
     ragged: bool = False
     extra: dict = field(default_factory=dict)
 
@@ -137,6 +141,10 @@ WORKLOADS = {
     "prefill_chunk_b4_t512": Workload(
         name="prefill_chunk_b4_t512", kind="chunk", seed=1008, dtype="bf16",
         B=4, T=512, Hq=48, Hkv=8, D=128, Tmax=8192),
+    # MoE FFN sub-layer: 4 x 2048 tokens, 8 experts 6144 -> 32768 -> 6144, top-2.
+    "moe_b4_t2048": Workload(
+        name="moe_b4_t2048", kind="moe", seed=1009, dtype="bf16",
+        B=4, T=2048, Hq=0, Hkv=0, D=0, d_model=6144, d_ffn=32768, n_experts=8, top_k=2),
 }
 
 
@@ -235,6 +243,31 @@ def make_chunk_inputs(B, T, Hq, Hkv, D, Tmax, seed, offsets=None):
             "step": step}
 
 
+def make_moe_inputs(B, T, d_model, d_ffn, n_experts, seed, scale_up=0.02 / 127, scale_down=0.02 / 127,
+                    router_std=None, distinct_scales=False):
+    """x [B,T,d] bf16; router weights [d, E] float32 N(0, router_std^2)
+    (default 1.5/sqrt(d): logits of standard deviation 1.5 for unit-RMS rows);
+    per expert the int8 weights Wg, Wv [d, F] and W1 [F, d] (uniform in
+    [-127, 127]) with float32 per-channel scales."""
+    g = rng(seed)
+    x = normal_bf16(g, (B, T, d_model))
+    std = router_std if router_std is not None else 1.5 / math.sqrt(d_model)
+    w_router = (normal_f32(g, (d_model, n_experts)) * np.float32(std)).astype(np.float32)
+
+    def sc(n, s):
+        if distinct_scales:
+            return (s * g.uniform(0.5, 1.5, size=n)).astype(np.float32)
+        return np.full(n, s, dtype=np.float32)
+
+    experts = []
+    for _ in range(n_experts):
+        wg = int8_uniform(g, (d_model, d_ffn))
+        wv = int8_uniform(g, (d_model, d_ffn))
+        w1 = int8_uniform(g, (d_ffn, d_model))
+        experts.append((wg, sc(d_ffn, scale_up), wv, sc(d_ffn, scale_up), w1, sc(d_model, scale_down)))
+    return {"x": x, "w_router": w_router, "experts": experts}
+
+
 def make_workload(name: str) -> dict:
     """All inputs of one named workload at its full size."""
     w = WORKLOADS[name]
@@ -242,6 +275,8 @@ def make_workload(name: str) -> dict:
         return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.seed, w.dtype)
     if w.kind == "decode":
         return make_decode_inputs(w.B, w.Hq, w.Hkv, w.D, w.Tmax, w.seed, ragged=w.ragged)
+    if w.kind == "moe":
+        return make_moe_inputs(w.B, w.T, w.d_model, w.d_ffn, w.n_experts, w.seed)
     if w.kind == "chunk":
         return make_chunk_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.Tmax, w.seed)
     if w.kind == "decode_sublayer":

@@ -57,6 +57,10 @@ __all__ = [
     "sublayer",
     "decode_sublayer",
     "chunk_prefill",
+    "gelu",
+    "moe_route",
+    "expert_ffn",
+    "moe_sublayer",
     "kv_cache_bytes",
 ]
 
@@ -363,6 +367,65 @@ def chunk_prefill(k_cache, v_cache, q, k_new, v_new, step, mult, cap=30.0, base=
     mask = attention_mask(pos, Tmax, kv_len=new_step)
     o = attention(qr, kc, vc, mask, mult, cap, out=io)
     return o, kc, vc, new_step
+
+
+def gelu(x):
+    """GELU in the tanh form ([ch6] §6.2 calls jax.nn.gelu, whose default is this
+    approximation): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def moe_route(n, w_router, k=2):
+    """Router ([ch3] §3.5; [ch2] §2.2): logits n @ W_r with a float32 weight
+    matrix [d, E], softmax over the E experts, the k most probable experts.
+
+    Returns (probs [..., E], idx [..., k] int64, gates [..., k]): gates are the
+    selected softmax probabilities themselves, not renormalised ([ch2] §2.5.1).
+    Ties keep the lower expert index first.
+    """
+    logits = np.asarray(n, np.float64) @ np.asarray(w_router, np.float64)
+    probs = softmax(logits, axis=-1)
+    idx = np.argsort(-probs, axis=-1, kind="stable")[..., :k]
+    gates = np.take_along_axis(probs, idx, axis=-1)
+    return probs, idx, gates
+
+
+def expert_ffn(n, wg, sg, wv, sv, w1, s1, io="bf16"):
+    """One expert, the gated FFN of [ch6] §6.2: (gelu(n Wg) * (n Wv)) W1 with
+    int8 Linears (Wg, Wv [d, F]; W1 [F, d]). The two up projections are handed
+    on in the I/O dtype, gelu(g) * v is rounded once, the down projection too."""
+    g = linear_int8(n, wg, sg, out=io)
+    v = linear_int8(n, wv, sv, out=io)
+    h = round_to(gelu(g) * v, io)
+    return linear_int8(h, w1, s1, out=io)
+
+
+def moe_sublayer(x, w_router, experts, eps=1e-5, k=2, io="bf16", idx=None):
+    """The FFN half of a decoder layer ([ch6] §6.3.1 sandwich norm; [ch2] §2.2):
+    n = norm(x); the k routed experts' outputs weighted by their gates and
+    summed (rounded once); y = x + norm(sum). No token is dropped (every token
+    goes to k experts). `experts` is a list of (wg, sg, wv, sv, w1, s1).
+    `idx` ([..., k]) may force the expert choice (for comparisons where the
+    router's top-k is tied within rounding). Returns (y, idx, gates)."""
+    n = rmsnorm(x, None, eps, out=io)
+    probs, idx0, gates = moe_route(n, w_router, k)
+    if idx is None:
+        idx = idx0
+    else:
+        idx = np.asarray(idx)
+        gates = np.take_along_axis(probs, idx, axis=-1)
+    lead = x.shape[:-1]
+    nf = n.reshape(-1, n.shape[-1])
+    idf = idx.reshape(-1, k)
+    gf = gates.reshape(-1, k)
+    acc = np.zeros_like(nf)
+    for e, ex in enumerate(experts):
+        rows, slots = np.nonzero(idf == e)
+        if rows.size:
+            acc[rows] += gf[rows, slots][:, None] * expert_ffn(nf[rows], *ex, io=io)
+    mix = round_to(acc.reshape(*lead, -1), io)
+    return rmsnorm(mix, None, eps, residual=x, out=io), idx, gates
 
 
 def kv_cache_bytes(num_layers, batch, seq_len, num_kv_heads, head_size, elem_bytes=2):

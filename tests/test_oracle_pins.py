@@ -498,3 +498,75 @@ def test_chunk_prefill_of_one_token_is_a_decode_step():
     b = orc.decode_step(kc, vc, q, k, v, step, 0.2, io=None)
     for x, y in zip(a, b):
         np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-14)
+
+
+def test_gelu_tanh_form():
+    """The tanh form: odd part exactly x (gelu(x) - gelu(-x) = x), gelu(0) = 0,
+    within 1e-3 of the exact erf form (its published error bound is ~2e-4), and
+    the saturations x for large x, 0 for large negative x."""
+    from scipy.special import erf
+    x = np.linspace(-8, 8, 4001)
+    gx = orc.gelu(x)
+    np.testing.assert_allclose(gx - orc.gelu(-x), x, rtol=0, atol=1e-12)
+    assert orc.gelu(0.0) == 0.0
+    exact = 0.5 * x * (1 + erf(x / np.sqrt(2)))
+    assert np.max(np.abs(gx - exact)) < 1e-3
+    assert abs(orc.gelu(20.0) - 20.0) < 1e-12 and abs(orc.gelu(-20.0)) < 1e-12
+    # a transposed constant (0.5 outside vs inside) or a missing cube term would break these:
+    assert abs(orc.gelu(1.0) - 0.8411919906082768) < 1e-12
+
+
+def test_router_softmax_top2_unnormalised_gates():
+    g = np.random.default_rng(61)
+    n = g.standard_normal((50, 16))
+    w = g.standard_normal((16, 8)).astype(np.float32)
+    probs, idx, gates = orc.moe_route(n, w)
+    np.testing.assert_allclose(probs.sum(-1), 1.0, rtol=1e-12)
+    # the two largest probabilities, in decreasing order, gates not renormalised
+    srt = np.sort(probs, -1)[:, ::-1]
+    np.testing.assert_allclose(gates, srt[:, :2], rtol=0, atol=0)
+    assert np.all(gates.sum(-1) < 1.0)
+    assert np.all(idx[:, 0] != idx[:, 1])
+    # ties: lower index first
+    p2, i2, _ = orc.moe_route(np.zeros((1, 16)), w)
+    np.testing.assert_array_equal(i2[0], [0, 1])
+
+
+def test_moe_with_identical_experts_is_one_dense_ffn_scaled_by_the_gate_sum():
+    """E identical experts: the routed mixture equals the dense gated FFN times
+    (g1 + g2); a single expert with weight 1 reduces to the dense block."""
+    g = np.random.default_rng(62)
+    T, d, F, E = 7, 32, 48, 4
+    x = orc.round_bf16(g.standard_normal((1, T, d)))
+    wr = (g.standard_normal((d, E)) * 0.3).astype(np.float32)
+    ex = (g.integers(-127, 128, (d, F), dtype=np.int8), np.full(F, 0.02 / 127, np.float32),
+          g.integers(-127, 128, (d, F), dtype=np.int8), np.full(F, 0.03 / 127, np.float32),
+          g.integers(-127, 128, (F, d), dtype=np.int8), np.full(d, 0.05 / 127, np.float32))
+    y, idx, gates = orc.moe_sublayer(x, wr, [ex] * E, io=None)
+    n = orc.rmsnorm(x, None, 1e-5)
+    dense = orc.expert_ffn(n, *ex, io=None)
+    mix = dense * gates.sum(-1)[..., None]
+    np.testing.assert_allclose(y, x + orc.rmsnorm(mix, None, 1e-5), rtol=1e-10, atol=1e-10)
+    # forcing the choice to expert 0 for both slots doubles its gate
+    y0, _, g0 = orc.moe_sublayer(x, wr, [ex] * E, io=None, idx=np.zeros((1, T, 2), np.int64))
+    p, _, _ = orc.moe_route(n, wr)
+    np.testing.assert_allclose(g0, np.repeat(p[..., :1], 2, -1), rtol=1e-15)
+
+
+def test_moe_routes_each_token_to_its_own_experts():
+    """Distinct experts: token t's output uses exactly experts idx[t] (checked
+    against a per-token sum written out separately)."""
+    g = np.random.default_rng(63)
+    T, d, F, E = 6, 16, 24, 4
+    x = orc.round_bf16(g.standard_normal((1, T, d)))
+    wr = (g.standard_normal((d, E)) * 0.5).astype(np.float32)
+    exps = [(g.integers(-127, 128, (d, F), dtype=np.int8), (0.02 / 127 * g.uniform(0.5, 1.5, F)).astype(np.float32),
+             g.integers(-127, 128, (d, F), dtype=np.int8), (0.02 / 127 * g.uniform(0.5, 1.5, F)).astype(np.float32),
+             g.integers(-127, 128, (F, d), dtype=np.int8), (0.05 / 127 * g.uniform(0.5, 1.5, d)).astype(np.float32))
+            for _ in range(E)]
+    y, idx, gates = orc.moe_sublayer(x, wr, exps, io=None)
+    n = orc.rmsnorm(x, None, 1e-5)[0]
+    for t in range(T):
+        mix = sum(gates[0, t, k] * orc.expert_ffn(n[t:t + 1], *exps[idx[0, t, k]], io=None)[0] for k in range(2))
+        np.testing.assert_allclose(y[0, t], x[0, t] + orc.rmsnorm(mix, None, 1e-5), rtol=1e-10, atol=1e-10)
+    assert len(np.unique(idx)) > 2  # the tokens do not all pick the same pair
