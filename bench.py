@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default="", help="comma list of prefill,decode_b1,decode_ragged,sublayer,"
-                    "decode_sublayer_b1,decode_sublayer_b32,chunk (default: all)")
+                    "decode_sublayer_b1,decode_sublayer_b32,chunk,moe (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (HBM counter calibration)")
@@ -240,6 +240,31 @@ def bench_chunk(torch, grok, pipe, U, gi, steps, warmup, replicas=2):
             "kernel_ms": kern_ms, "kernel_tflops": flop / (kern_ms * 1e-3) / 1e12}
 
 
+def bench_moe(torch, grok, pipe, U, gi, steps, warmup):
+    """One step = the MoE FFN sub-layer over 8192 token rows: norm, router,
+    routing plan, the two grouped int8 expert products (GeGLU up projection of
+    the gathered rows, down projection), gate-weighted combine, norm, residual.
+    Counted work: the expert products, 6 * T * k * d * F flop."""
+    w = gi.WORKLOADS["moe_b4_t2048"]
+    p = gi.make_workload(w.name)
+    T, d, F = w.B * w.T, w.d_model, w.d_ffn
+    x = U.dev_bf16(p["x"].reshape(T, d))
+    experts = [tuple(U.dev(a) for a in ex) for ex in p["experts"]]
+    wr = U.dev(p["w_router"])
+    del p
+    step = pipe.MoeStep(x, wr, experts, k=w.top_k)
+    del experts
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    flop = 6 * T * w.top_k * d * F
+    sec = time_steps(torch, pipe, [step], steps, warmup)
+    kern_ms = time_kernel(torch, lambda i: step(), max(2, steps // 2))
+    counts = np.bincount(step.idx.cpu().numpy().ravel(), minlength=w.n_experts)
+    return {"workload": w.name, "ms_per_step": sec * 1e3, "value": flop / sec / 1e12, "unit": "TFLOP/s",
+            "flop_per_step": flop, "rows_per_expert": counts.tolist(), "kernel": "moe_ffn (all kernels)",
+            "kernel_ms": kern_ms, "kernel_tflops": flop / (kern_ms * 1e-3) / 1e12}
+
+
 def cpu_baseline(gi, orc):
     """The fp64 oracle on a bounded sample of the 8k prefill: all 48 heads of
     256 query rows spread over the sequence (RoPE of the sampled q rows and of
@@ -286,7 +311,7 @@ def main():
     import gpu_util as U
 
     only = set(args.only.split(",")) if args.only else {"prefill", "decode_b1", "decode_ragged", "sublayer",
-                                                        "decode_sublayer_b1", "decode_sublayer_b32", "chunk"}
+                                                        "decode_sublayer_b1", "decode_sublayer_b32", "chunk", "moe"}
     res = {}
     if args.copy_calibration:
         # a plain copy of known size: reads and writes exactly 256 MiB
@@ -324,6 +349,10 @@ def main():
     if "chunk" in only:
         res["chunk"] = bench_chunk(torch, grok, pipe, U, gi, args.steps, args.warmup)
         print(f"# chunk done: {res['chunk']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "moe" in only:
+        res["moe"] = bench_moe(torch, grok, pipe, U, gi, max(2, args.steps // 10), min(args.warmup, 4))
+        print(f"# moe done: {res['moe']['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     head = res.get("prefill") or next(iter(res.values()))
     line = {

@@ -23,7 +23,8 @@ __all__ = [
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
     "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
-    "grok_attn_decode_workspace_bytes",
+    "grok_attn_decode_workspace_bytes", "grok_moe_workspace_bytes", "grok_moe_interleave",
+    "grok_moe_route", "grok_moe_ffn",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrokattn.so")
@@ -57,6 +58,10 @@ _PROTOS = {
     "grok_attn_prefill_chunk": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _p]),
     "grok_attn_decode_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i,
                                      _f, _f, _f, _p]),
+    "grok_moe_workspace_bytes": (_sz, [_i64, _i, _i, _i, _i]),
+    "grok_moe_interleave": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _p]),
+    "grok_moe_route": (_i, [_p, _p, _p, _p, _i64, _i, _i, _i, _p]),
+    "grok_moe_ffn": (_i, [_p, _p, _i, _i, _p, _p, _p, _p, _i64, _i, _i, _f, _p, _p, _p, _sz, _p, _p]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _fn = getattr(lib, _name)
@@ -324,4 +329,84 @@ def grok_attn_prefill_chunk(q, k_cache, v_cache, offset, out, attn_mult, softcap
     _check(lib.grok_attn_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(offset), _ptr(out),
                                        _ptr(status), B, T, Tmax, Hq, Hkv, D, attn_mult, softcap, _stream(q)),
            "grok_attn_prefill_chunk")
+    return out
+
+
+def grok_moe_workspace_bytes(T, d, F, E, k) -> int:
+    return lib.grok_moe_workspace_bytes(T, d, F, E, k)
+
+
+def grok_moe_interleave(wg, sg, wv, sv, wgv=None, sgv=None):
+    """Gate and value up-projection weights of one expert side by side in blocks
+    of four columns (the form grok_moe_ffn reads): wgv [d, 2F], sgv [2F]."""
+    _need(wg, "wg", torch.int8, 2)
+    _need(wv, "wv", torch.int8, 2)
+    _need(sg, "sg", torch.float32, 1)
+    _need(sv, "sv", torch.float32, 1)
+    d, F = wg.shape
+    if wv.shape != (d, F) or sg.shape != (F,) or sv.shape != (F,):
+        raise ValueError("wg, wv [d, F] and sg, sv [F] must match")
+    if wgv is None:
+        wgv = torch.empty(d, 2 * F, dtype=torch.int8, device=wg.device)
+    if sgv is None:
+        sgv = torch.empty(2 * F, dtype=torch.float32, device=wg.device)
+    _need(wgv, "wgv", torch.int8)
+    _need(sgv, "sgv", torch.float32)
+    if wgv.numel() != 2 * d * F or sgv.numel() != 2 * F:
+        raise ValueError("wgv must hold d*2F bytes and sgv 2F floats")
+    _check(lib.grok_moe_interleave(_ptr(wg), _ptr(sg), _ptr(wv), _ptr(sv), _ptr(wgv), _ptr(sgv), d, F,
+                                   _stream(wg)), "grok_moe_interleave")
+    return wgv, sgv
+
+
+def grok_moe_route(n, w_router, idx, gates):
+    """idx, gates [T, k] = the k most probable experts of softmax(n @ w_router)
+    (fp32) and their probabilities; n [T, d] bf16 normalised rows."""
+    _need(n, "n", torch.bfloat16)
+    _need(w_router, "w_router", torch.float32, 2)
+    _need(idx, "idx", torch.int32)
+    _need(gates, "gates", torch.float32)
+    d, E = w_router.shape
+    T = n.numel() // d
+    k = idx.shape[-1]
+    if idx.numel() != T * k or gates.numel() != T * k:
+        raise ValueError("idx and gates must be [T, k]")
+    _check(lib.grok_moe_route(_ptr(n), _ptr(w_router), _ptr(idx), _ptr(gates), T, d, E, k, _stream(n)),
+           "grok_moe_route")
+    return idx, gates
+
+
+def grok_moe_ffn(x, w_router, wgv, sgv, w1, s1, out, workspace, k=2, eps=1e-5, idx=None, gates=None):
+    """out [T, d] = x + norm(sum over the k routed experts of gate * expert(norm(x)))
+    with GeGLU experts (wgv[e], sgv[e] from grok_moe_interleave; w1[e] [F, d],
+    s1[e] [d]); idx, gates [T, k] optional outputs of the routing."""
+    _need(x, "x", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    _need(w_router, "w_router", torch.float32, 2)
+    _need(workspace, "workspace")
+    _need(idx, "idx", torch.int32)
+    _need(gates, "gates", torch.float32)
+    d, E = w_router.shape
+    T = x.numel() // d
+    if out.numel() != T * d:
+        raise ValueError("out must match x")
+    if not (len(wgv) == len(sgv) == len(w1) == len(s1) == E):
+        raise ValueError(f"need {E} experts' weights")
+    F = w1[0].shape[0]
+    for e in range(E):
+        _need(wgv[e], f"wgv[{e}]", torch.int8)
+        _need(sgv[e], f"sgv[{e}]", torch.float32, 1)
+        _need(w1[e], f"w1[{e}]", torch.int8, 2)
+        _need(s1[e], f"s1[{e}]", torch.float32, 1)
+        if wgv[e].numel() != 2 * d * F or sgv[e].numel() != 2 * F or tuple(w1[e].shape) != (F, d) \
+                or s1[e].numel() != d:
+            raise ValueError(f"expert {e}: weight sizes do not match d={d} F={F}")
+    for t, name in ((idx, "idx"), (gates, "gates")):
+        if t is not None and t.numel() != T * k:
+            raise ValueError(f"{name} must be [T, k]")
+    arr = lambda ts: ctypes.cast((_p * E)(*[_ptr(t) for t in ts]), _p)
+    _check(lib.grok_moe_ffn(_ptr(x), _ptr(w_router), E, k, arr(wgv), arr(sgv), arr(w1), arr(s1), T, d, F,
+                            eps, _ptr(idx), _ptr(gates), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _ptr(out), _stream(x)),
+           "grok_moe_ffn")
     return out

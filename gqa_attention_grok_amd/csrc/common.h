@@ -76,6 +76,34 @@ hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, 
                             const RopeFreqs &f, hipStream_t s);
 hipError_t launch_linear_int8(const void *x, const int8_t *w, const float *scales, void *y,
                               int64_t M, int K, int N, hipStream_t s);
+// Grouped (MoE) form of the tiled int8 GEMM: kMaxGroups groups at most.
+constexpr int kMaxGroups = 8;
+struct GroupArgs {
+  const int32_t *offsets;  // [E + 1] device: group e owns rows [offsets[e], offsets[e+1])
+  const int32_t *rows;     // [M] device: x row of each grouped row, or NULL
+  const int8_t *w[kMaxGroups];
+  const float *s[kMaxGroups];
+  int E;
+};
+hipError_t launch_linear_int8_grouped(const void *x, const int32_t *rows, const int32_t *offsets, int E,
+                                      const int8_t *const *w, const float *const *scales, void *y,
+                                      int64_t M_total, int K, int N, bool geglu, hipStream_t s);
+// MoE FFN sub-layer (moe.hip): workspace byte offsets of its intermediates.
+struct MoeWorkspace {
+  size_t n, idx, gates, offsets, rows, pos, h, y, total;
+};
+MoeWorkspace moe_workspace(int64_t T, int d, int F, int E, int k);
+int moe_max_experts();
+int moe_max_k();
+int moe_max_width();
+hipError_t launch_moe_route(const void *n, const float *wr, int32_t *idx, float *gates, int64_t T, int d, int E,
+                            int k, hipStream_t s);
+hipError_t launch_moe_interleave(const int8_t *wg, const int8_t *wv, const float *sg, const float *sv,
+                                 int8_t *wgv, float *sgv, int K, int F, hipStream_t s);
+hipError_t launch_moe_ffn(const void *x, const float *w_router, int E, int k, const int8_t *const *wgv,
+                          const float *const *sgv, const int8_t *const *w1, const float *const *s1, int64_t T,
+                          int d, int F, float eps, int32_t *idx, float *gates, void *workspace, void *out,
+                          hipStream_t s);
 // Few-row int8 Linear on packed weights (layout in linear_int8_gemv.hip).
 size_t gemv_packed_bytes(int K, int N);
 hipError_t launch_linear_int8_pack(const int8_t *w, int8_t *wp, int K, int N, hipStream_t s);

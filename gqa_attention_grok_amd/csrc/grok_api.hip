@@ -294,4 +294,81 @@ int grok_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_ca
                     "attn_prefill_chunk");
 }
 
+namespace {
+
+// Shared shape checks of the MoE entry points; 0 when fine.
+int moe_shape_error(const char *who, int64_t T, int d, int F, int E, int k) {
+  if (T < 0 || d < 8 || d % 8 || F < 8 || F % 8)
+    return fail(GROK_EINVAL, "%s: bad shape T=%lld d=%d F=%d (d, F positive multiples of 8)", who,
+                (long long)T, d, F);
+  if (E < 1 || E > grok::moe_max_experts())
+    return fail(GROK_EINVAL, "%s: E=%d outside [1, %d]", who, E, grok::moe_max_experts());
+  if (k < 1 || k > E || k > grok::moe_max_k())
+    return fail(GROK_EINVAL, "%s: k=%d outside [1, min(E, %d)]", who, k, grok::moe_max_k());
+  if (d > grok::moe_max_width()) return fail(GROK_EINVAL, "%s: d=%d above %d", who, d, grok::moe_max_width());
+  // gathered rows are addressed with 32-bit byte offsets; entries are int32
+  if (T * d * 2 >= (int64_t(1) << 32) || T * k > 0x7fffffff)
+    return fail(GROK_EINVAL, "%s: T=%lld too large", who, (long long)T);
+  if ((T * k + 255) / 256 + E > 65535 || static_cast<int64_t>(d) * F * 2 >= (int64_t(1) << 32))
+    return fail(GROK_EINVAL, "%s: T=%lld or F=%d too large", who, (long long)T, F);
+  return 0;
+}
+
+}  // namespace
+
+size_t grok_moe_workspace_bytes(int64_t T, int d, int F, int E, int k) {
+  if (T < 0 || d < 1 || F < 1 || E < 1 || k < 1) return 0;
+  return grok::moe_workspace(T, d, F, E, k).total;
+}
+
+int grok_moe_interleave(const int8_t *wg, const float *sg, const int8_t *wv, const float *sv, int8_t *wgv,
+                        float *sgv, int d, int F, hipStream_t stream) {
+  if (d < 1 || F < 8 || F % 8) return fail(GROK_EINVAL, "moe_interleave: bad shape d=%d F=%d", d, F);
+  if (static_cast<int64_t>(d) * F * 2 >= (int64_t(1) << 32)) return fail(GROK_EINVAL, "moe_interleave: too large");
+  if (!wg || !sg || !wv || !sv || !wgv || !sgv) return fail(GROK_EINVAL, "moe_interleave: null pointer");
+  if ((reinterpret_cast<uintptr_t>(wg) | reinterpret_cast<uintptr_t>(wv)) % 4 ||
+      reinterpret_cast<uintptr_t>(wgv) % 8 ||
+      (reinterpret_cast<uintptr_t>(sg) | reinterpret_cast<uintptr_t>(sv) | reinterpret_cast<uintptr_t>(sgv)) % 16)
+    return fail(GROK_EINVAL, "moe_interleave: misaligned pointer");
+  return hip_status(grok::launch_moe_interleave(wg, wv, sg, sv, wgv, sgv, d, F, stream), "moe_interleave");
+}
+
+int grok_moe_route(const void *n, const float *w_router, int32_t *idx, float *gates, int64_t T, int d,
+                   int E, int k, hipStream_t stream) {
+  if (int r = moe_shape_error("moe_route", T, d, 8, E, k)) return r;
+  if (T == 0) return ok();
+  if (!n || !w_router || !idx || !gates) return fail(GROK_EINVAL, "moe_route: null pointer");
+  if (reinterpret_cast<uintptr_t>(n) % 16 ||
+      (reinterpret_cast<uintptr_t>(w_router) | reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(gates)) % 4)
+    return fail(GROK_EINVAL, "moe_route: misaligned pointer");
+  return hip_status(grok::launch_moe_route(n, w_router, idx, gates, T, d, E, k, stream), "moe_route");
+}
+
+int grok_moe_ffn(const void *x, const float *w_router, int E, int k, const int8_t *const *wgv,
+                 const float *const *sgv, const int8_t *const *w1, const float *const *s1, int64_t T, int d,
+                 int F, float eps, int32_t *idx, float *gates, void *workspace, size_t ws_bytes, void *out,
+                 hipStream_t stream) {
+  if (int r = moe_shape_error("moe_ffn", T, d, F, E, k)) return r;
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(GROK_EINVAL, "moe_ffn: bad eps");
+  if (T == 0) return ok();
+  if (!x || !w_router || !wgv || !sgv || !w1 || !s1 || !workspace || !out)
+    return fail(GROK_EINVAL, "moe_ffn: null pointer");
+  uintptr_t a16 = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out) |
+                  reinterpret_cast<uintptr_t>(workspace);
+  uintptr_t a8 = 0;
+  for (int e = 0; e < E; ++e) {
+    if (!wgv[e] || !sgv[e] || !w1[e] || !s1[e]) return fail(GROK_EINVAL, "moe_ffn: null pointer in expert %d", e);
+    a16 |= reinterpret_cast<uintptr_t>(sgv[e]) | reinterpret_cast<uintptr_t>(s1[e]);
+    a8 |= reinterpret_cast<uintptr_t>(wgv[e]) | reinterpret_cast<uintptr_t>(w1[e]);
+  }
+  const uintptr_t a4 = reinterpret_cast<uintptr_t>(w_router) | reinterpret_cast<uintptr_t>(idx) |
+                       reinterpret_cast<uintptr_t>(gates);
+  if (a16 % 16 || a8 % 8 || a4 % 4) return fail(GROK_EINVAL, "moe_ffn: misaligned pointer");
+  const size_t need = grok::moe_workspace(T, d, F, E, k).total;
+  if (ws_bytes < need) return fail(GROK_ENOMEM, "moe_ffn: workspace %zu bytes < %zu needed", ws_bytes, need);
+  return hip_status(grok::launch_moe_ffn(x, w_router, E, k, wgv, sgv, w1, s1, T, d, F, eps, idx, gates, workspace,
+                                         out, stream),
+                    "moe_ffn");
+}
+
 }  // extern "C"

@@ -88,9 +88,26 @@ __device__ __forceinline__ void lds_wait(bf16x8 (&a)[4], bf16x8 (&b)[4]) {
                : "i"(kLeft));
 }
 
+// tanh form of GELU in fp32: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
+// tanh(u) = 1 - 2 / (1 + exp(2u)) (saturates correctly at both ends).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  const float t = 1.f - 2.f / (1.f + __expf(2.f * u));
+  return 0.5f * x * (1.f + t);
+}
+
+// kGrouped: the rows of y are grouped by expert (MoE, grouped GEMM): group e
+// owns rows [ga.offsets[e], ga.offsets[e+1]) and is multiplied by its own
+// weights ga.w[e], scales ga.s[e]; blockIdx.y enumerates the row tiles of the
+// groups in order (tiles past the last group exit). kGather: row m of x is
+// row ga.rows[m] of the x buffer (the token a grouped row stands for).
+// kGeGLU: the weight columns hold gate and value channels interleaved by four
+// (columns 8q..8q+3 = gate channels 4q..4q+3, 8q+4..8q+7 = value channels),
+// and the epilogue writes h = gelu(gate) * value into y [M, N/2].
+template <bool kGrouped, bool kGather, bool kGeGLU>
 __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
-    const bf16_t *__restrict__ x, const int8_t *__restrict__ w, const float *__restrict__ scales,
-    bf16_t *__restrict__ y, int64_t M, int K, int N) {
+    const bf16_t *__restrict__ x, const int8_t *__restrict__ w_in, const float *__restrict__ scales_in,
+    bf16_t *__restrict__ y, int64_t M, int K, int N, GroupArgs ga) {
   __shared__ __attribute__((aligned(1024))) unsigned char Xs[3][kXTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char Wt[2][kTileB];
 
@@ -100,7 +117,28 @@ __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
   const int lr = lane % 16, lg = lane / 16;
   const int wn = wave % 2, wm = wave / 2;
   const int n0 = blockIdx.x * kBN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
+  int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
+  const int8_t *w = w_in;
+  const float *scales = scales_in;
+  if constexpr (kGrouped) {
+    // this tile's group: walk the groups' tile counts (uniform, scalar loads)
+    int ty = blockIdx.y, e = -1;
+    int64_t lo = 0;
+    for (int q = 0; q < ga.E; ++q) {
+      const int o0 = ga.offsets[q], o1 = ga.offsets[q + 1];
+      const int nt = (o1 - o0 + kBM - 1) / kBM;
+      if (e < 0 && ty < nt) {
+        e = q;
+        m0 = o0 + static_cast<int64_t>(ty) * kBM;
+        lo = o1;
+      }
+      if (e < 0) ty -= nt;
+    }
+    if (e < 0) return;  // whole workgroup: past the last group's tiles
+    M = lo;             // the group's end row
+    w = ga.w[e];
+    scales = ga.s[e];
+  }
 
   // X tile: HBM -> LDS directly (global_load_lds, 16 bytes per lane). Wave
   // `wave`, instruction i fills rows 32*wave + 8*i .. +7; lane L writes chunk
@@ -114,9 +152,13 @@ __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 32 * wave + 8 * i + xl_row;
-    xoff[i] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2) + 16 * (xl_pos ^ sw(r));
+    if constexpr (kGather)
+      xoff[i] = static_cast<uint32_t>(static_cast<int64_t>(ga.rows[min(m0 + r, M - 1)]) * K * 2) +
+                16 * (xl_pos ^ sw(r));
+    else
+      xoff[i] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2) + 16 * (xl_pos ^ sw(r));
   }
-  const char *xtile = reinterpret_cast<const char *>(x + m0 * K);
+  const char *xtile = reinterpret_cast<const char *>(kGather ? x : x + m0 * K);
   auto issue_x = [&](int k0, int buf) {
     if (k0 + kBK <= K) {
 #pragma unroll
@@ -128,7 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 32 * wave + 8 * i + xl_row;
-      const int64_t m = min(m0 + r, M - 1);
+      const int64_t mr = min(m0 + r, M - 1);
+      const int64_t m = kGather ? static_cast<int64_t>(ga.rows[mr]) : mr;
       const int k = min(k0 + 8 * (xl_pos ^ sw(r)), K - 8);
       __builtin_amdgcn_global_load_lds(x + m * K + k, (lds_void *)(&Xs[buf][(32 * wave + 8 * i) * kRowB]), 16,
                                        0, 0);
@@ -265,6 +308,35 @@ __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   // Epilogue: lane holds Y^T[n = nbase + 4*lg + v, m = mbase + lr], v = 0..3.
+  if constexpr (kGeGLU) {
+    // lanes lg and lg ^ 1 hold the gate and the value columns of the same 4
+    // channels: the even one combines and stores them. Both projections are
+    // rounded to bf16 (as a separate projection would hand them on), then
+    // gelu(gate) * value is rounded once.
+    const int Nh = N / 2;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + 64 * wn + 16 * nb + 4 * lg;  // lg even: gate columns, n % 8 == 0
+      const bool ok_n = n < N;
+      const f32x4 sc = ok_n ? *reinterpret_cast<const f32x4 *>(scales + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const f32x4 v = acc[nb][mb];
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = bf16_to_f32(f32_to_bf16(v[e] * sc[e]));
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __shfl_xor(r[e], 16, kWave);
+        const int64_t m = m0 + 64 * wm + 16 * mb + lr;
+        if ((lg & 1) || !ok_n || m >= M) continue;
+        const u32x2 hw = {cvt_pk_bf16(gelu_tanh(r[0]) * o[0], gelu_tanh(r[1]) * o[1]),
+                          cvt_pk_bf16(gelu_tanh(r[2]) * o[2], gelu_tanh(r[3]) * o[3])};
+        *reinterpret_cast<u32x2 *>(y + m * Nh + n / 2) = hw;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int n = n0 + 64 * wn + 16 * nb + 4 * lg;
@@ -288,8 +360,40 @@ hipError_t launch_linear_int8(const void *x, const int8_t *w, const float *scale
   const int64_t gm = (M + kBM - 1) / kBM;
   if (gm > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((N + kBN - 1) / kBN, static_cast<unsigned>(gm));
-  hipLaunchKernelGGL(linear_int8_kernel, grid, dim3(kThreads), 0, s,
-                     static_cast<const bf16_t *>(x), w, scales, static_cast<bf16_t *>(y), M, K, N);
+  hipLaunchKernelGGL((linear_int8_kernel<false, false, false>), grid, dim3(kThreads), 0, s,
+                     static_cast<const bf16_t *>(x), w, scales, static_cast<bf16_t *>(y), M, K, N, GroupArgs{});
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_int8_grouped(const void *x, const int32_t *rows, const int32_t *offsets, int E,
+                                      const int8_t *const *w, const float *const *scales, void *y,
+                                      int64_t M_total, int K, int N, bool geglu, hipStream_t s) {
+  GroupArgs ga = {};
+  ga.offsets = offsets;
+  ga.rows = rows;
+  ga.E = E;
+  for (int e = 0; e < E; ++e) {
+    ga.w[e] = w[e];
+    ga.s[e] = scales[e];
+  }
+  // row tiles: at most one partial tile per group beyond the full ones
+  const int64_t gm = (M_total + kBM - 1) / kBM + E;
+  if (gm > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((N + kBN - 1) / kBN, static_cast<unsigned>(gm));
+  const bf16_t *xb = static_cast<const bf16_t *>(x);
+  bf16_t *yb = static_cast<bf16_t *>(y);
+  if (rows && geglu)
+    hipLaunchKernelGGL((linear_int8_kernel<true, true, true>), grid, dim3(kThreads), 0, s, xb, w[0], scales[0], yb,
+                       M_total, K, N, ga);
+  else if (rows)
+    hipLaunchKernelGGL((linear_int8_kernel<true, true, false>), grid, dim3(kThreads), 0, s, xb, w[0], scales[0], yb,
+                       M_total, K, N, ga);
+  else if (geglu)
+    hipLaunchKernelGGL((linear_int8_kernel<true, false, true>), grid, dim3(kThreads), 0, s, xb, w[0], scales[0], yb,
+                       M_total, K, N, ga);
+  else
+    hipLaunchKernelGGL((linear_int8_kernel<true, false, false>), grid, dim3(kThreads), 0, s, xb, w[0], scales[0],
+                       yb, M_total, K, N, ga);
   return hipGetLastError();
 }
 

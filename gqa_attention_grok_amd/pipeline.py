@@ -19,6 +19,10 @@ owns device memory).
   against the KV memory (ch. 4 §4.4, ch. 6 §6.6): the projections are few-row
   products that stream the int8 weights once, and the attention is the
   one-token decode over slots [0, step[b]+1).
+* ``MoeStep``      -- the FFN half of a decoder layer (ch. 6 §6.2, §6.3.1;
+  ch. 3 "Configuration and hyperparameters" §3.5; ch. 2 "Overall
+  architecture" §2.2): y = x + norm(sum of the two routed GeGLU experts'
+  outputs, weighted by their router probabilities) -- one call.
 """
 from __future__ import annotations
 
@@ -27,7 +31,8 @@ import torch
 from . import (grok_attn_decode, grok_attn_decode_append, grok_attn_decode_workspace_bytes,
                grok_attn_prefill, grok_attn_prefill_chunk,
                grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
-               grok_linear_int8_pack, grok_rmsnorm, grok_rope)
+               grok_linear_int8_pack, grok_moe_ffn, grok_moe_interleave, grok_moe_workspace_bytes,
+               grok_rmsnorm, grok_rope)
 
 
 def capture(step) -> "torch.cuda.CUDAGraph":
@@ -237,3 +242,31 @@ class DecodeSublayerStep:
         self.project_out()
         grok_rmsnorm(self.o, self.y, residual=self.x, eps=self.eps)
         return self.y
+
+
+class MoeStep:
+    """MoE FFN sub-layer: the experts' gate and value weights are interleaved
+    once at construction; each call is one grok_moe_ffn on preallocated
+    buffers. `experts` is a list of (wg, sg, wv, sv, w1, s1) device tensors."""
+
+    def __init__(self, x, w_router, experts, k=2, eps=1e-5):
+        self.x, self.w_router, self.k, self.eps = x, w_router, k, eps
+        d, E = w_router.shape
+        T = x.numel() // d
+        F = experts[0][4].shape[0]
+        dev = x.device
+        self.wgv, self.sgv, self.w1, self.s1 = [], [], [], []
+        for wg, sg, wv, sv, w1, s1 in experts:
+            a, b = grok_moe_interleave(wg, sg, wv, sv)
+            self.wgv.append(a)
+            self.sgv.append(b)
+            self.w1.append(w1)
+            self.s1.append(s1)
+        self.ws = torch.empty(grok_moe_workspace_bytes(T, d, F, E, k), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(x)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        return grok_moe_ffn(self.x, self.w_router, self.wgv, self.sgv, self.w1, self.s1, self.out, self.ws,
+                            k=self.k, eps=self.eps, idx=self.idx, gates=self.gates)

@@ -5,6 +5,7 @@
  *   [ch4] "model.py close reading, part 1: RMSNorm, RoPE, GQA Attention"
  *   [ch6] "model.py close reading, part 3: block assembly and sharding"
  *   [ch3] "Configuration and hyperparameters"
+ *   [ch2] "Overall architecture"
  * Section numbers below are the pages' own.
  *
  * Conventions shared by every entry point
@@ -294,6 +295,60 @@ GROK_API int grok_attn_decode_append(const void *q, const void *k_new, const voi
 
 /* Workspace bytes grok_attn_decode needs for these sizes (0 on bad sizes). */
 GROK_API size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D);
+
+/*
+ * MoE FFN sub-layer: the FFN half of a decoder layer ([ch6] §6.3.1 sandwich
+ * norm; [ch2] §2.2 data flow), for T token rows:
+ *   n     = rmsnorm(x)                          (unit scale, bf16)
+ *   p     = softmax(n @ w_router)               (fp32 logits and softmax, [ch3] §3.5)
+ *   idx   = the k most probable experts of each row (equal probabilities:
+ *           lower expert index first); gates = their probabilities, not
+ *           renormalised ([ch2] §2.5.1)
+ *   h_e   = bf16(gelu(bf16(n Wg_e)) * bf16(n Wv_e))   (tanh-form GELU, [ch6] §6.2)
+ *   mix   = bf16(sum over the k chosen e of gate * bf16(h_e W1_e))  (fp32 sum)
+ *   out   = bf16(x + bf16(rmsnorm(mix)))
+ * Every row goes to its k experts (no capacity limit, nothing dropped). The
+ * int8 Linears have the numerics of grok_linear_int8 (exact int8, fp32 sums,
+ * per-channel scale on the fp32 sum).
+ *
+ * grok_moe_interleave writes the up-projection weights of one expert in the
+ * form grok_moe_ffn reads: gate and value columns side by side in blocks of
+ * four,
+ *   wgv[r][8q + j] = wg[r][4q + j],  wgv[r][8q + 4 + j] = wv[r][4q + j]  (j < 4)
+ * and the same for the scales (sgv [2F]).
+ *   wg, wv [d, F] int8 (4-byte aligned); sg, sv [F] fp32 (16-byte aligned);
+ *   wgv [d, 2F] int8 (8-byte aligned); sgv [2F] fp32 (16-byte aligned).
+ *
+ * grok_moe_route: the router alone, on already normalised rows.
+ *   n [T, d] bf16 (16-byte aligned); w_router [d, E] fp32;
+ *   idx [T, k] int32 and gates [T, k] fp32 (outputs).
+ *
+ * grok_moe_ffn: the whole sub-layer.
+ *   x [T, d] bf16; w_router [d, E] fp32 (device);
+ *   wgv, sgv, w1, s1: host arrays of E device pointers: wgv[e] [d, 2F] int8 and
+ *     sgv[e] [2F] fp32 (grok_moe_interleave's output), w1[e] [F, d] int8,
+ *     s1[e] [d] fp32;
+ *   idx, gates: [T, k] int32 / fp32 device outputs, or NULL (then kept in
+ *     the workspace only);
+ *   workspace: device, 16-byte aligned, grok_moe_workspace_bytes(T, d, F, E, k)
+ *     bytes (normalised rows, routing plan, [T*k, F] and [T*k, d] bf16
+ *     intermediates); out [T, d] bf16, must not overlap x.
+ * Limits: 1 <= k <= E <= 8, k <= 4; d and F multiples of 8; d <= 8192;
+ * T*d*2 < 2^32. T == 0 is a no-op.
+ * Errors: EINVAL for NULL pointers, sizes outside the limits, a bad eps or a
+ * misaligned pointer (x, out, workspace, sgv[e], s1[e]: 16 bytes; wgv[e],
+ * w1[e]: 8; w_router, idx, gates: 4); ENOMEM if ws_bytes is too small.
+ */
+GROK_API size_t grok_moe_workspace_bytes(int64_t T, int d, int F, int E, int k);
+GROK_API int grok_moe_interleave(const int8_t *wg, const float *sg, const int8_t *wv, const float *sv,
+                                 int8_t *wgv, float *sgv, int d, int F, hipStream_t stream);
+GROK_API int grok_moe_route(const void *n, const float *w_router, int32_t *idx, float *gates,
+                            int64_t T, int d, int E, int k, hipStream_t stream);
+GROK_API int grok_moe_ffn(const void *x, const float *w_router, int E, int k,
+                          const int8_t *const *wgv, const float *const *sgv,
+                          const int8_t *const *w1, const float *const *s1, int64_t T, int d, int F,
+                          float eps, int32_t *idx, float *gates, void *workspace, size_t ws_bytes,
+                          void *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 20, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -255,3 +255,48 @@ def test_prefill_chunk_validation(lib):
     assert call(cap=0.0) == EINVAL
     assert call(off=None) == EINVAL
     assert call(q=ctypes.c_void_p(0x10004)) == EINVAL
+
+
+def test_moe_validation_and_workspace(lib):
+    wsb = lambda T, d, F, E, k: _c(lib, "grok_moe_workspace_bytes", ctypes.c_int64(T), i(d), i(F), i(E), i(k),
+                                   restype=ctypes.c_size_t)
+    # n, idx, gates, offsets, rows, pos, h [T*k, F], y [T*k, d]; each rounded up to 256 bytes
+    r = lambda b: (b + 255) // 256 * 256
+    T, d, F, E, k = 100, 64, 96, 8, 2
+    assert wsb(T, d, F, E, k) == (r(T * d * 2) + 4 * r(T * k * 4) + r((E + 1) * 4) + r(T * k * F * 2)
+                                  + r(T * k * d * 2))
+    assert wsb(-1, d, F, E, k) == 0
+
+    arr = (ctypes.c_void_p * 8)(*([0x10000] * 8))
+    parr = ctypes.cast(arr, ctypes.c_void_p)
+
+    def ffn(T=16, d=64, F=96, E=8, k=2, eps=1e-5, x=FAKE, ws_bytes=1 << 40, w=parr):
+        return _c(lib, "grok_moe_ffn", x, FAKE, i(E), i(k), w, parr, parr, parr, ctypes.c_int64(T), i(d), i(F),
+                  fl(eps), None, None, FAKE, ctypes.c_size_t(ws_bytes), FAKE, None)
+    assert ffn(E=9) == EINVAL and "E=9" in _err(lib)
+    assert ffn(k=3, E=2) == EINVAL
+    assert ffn(k=5) == EINVAL
+    assert ffn(d=60) == EINVAL
+    assert ffn(F=100) == EINVAL
+    assert ffn(d=8200) == EINVAL
+    assert ffn(T=1 << 30, d=4096) == EINVAL    # 32-bit gathered row offsets
+    assert ffn(eps=-1.0) == EINVAL
+    assert ffn(x=None) == EINVAL
+    assert ffn(x=ctypes.c_void_p(0x10008)) == EINVAL
+    assert ffn(w=None) == EINVAL
+    assert ffn(ws_bytes=16) == ENOMEM
+    assert ffn(T=0) == 0                       # no-op
+
+    def route(T=16, d=64, E=8, k=2, n=FAKE):
+        return _c(lib, "grok_moe_route", n, FAKE, FAKE, FAKE, ctypes.c_int64(T), i(d), i(E), i(k), None)
+    assert route(E=0) == EINVAL
+    assert route(k=0) == EINVAL
+    assert route(n=ctypes.c_void_p(0x10004)) == EINVAL
+    assert route(T=0) == 0
+
+    def inter(d=64, F=96, sg=FAKE):
+        return _c(lib, "grok_moe_interleave", FAKE, sg, FAKE, FAKE, FAKE, FAKE, i(d), i(F), None)
+    assert inter(F=4) == EINVAL
+    assert inter(d=0) == EINVAL
+    assert inter(sg=ctypes.c_void_p(0x10004)) == EINVAL
+    assert inter(sg=None) == EINVAL

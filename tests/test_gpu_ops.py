@@ -646,3 +646,135 @@ def test_decode_sublayer(G, B, d, Hq, Hkv, lens, Tmax, fused):
         U.assert_bf16_close(U.host(st.v_cache[b, s]), vc2[b, s], f"appended v b={b}")
     nt = ref - x
     U.assert_bf16_close(y, ref, "decode sub-layer", magnitude=np.maximum(np.abs(ref), np.abs(nt)))
+
+
+# --------------------------------------------------------------------------
+# MoE FFN sub-layer
+# --------------------------------------------------------------------------
+MOE_GATE_TOL = 1e-3
+
+
+def _moe_dev(U, p):
+    x = U.dev_bf16(p["x"])
+    wr = U.dev(p["w_router"])
+    experts = [tuple(U.dev(a) for a in ex) for ex in p["experts"]]
+    return x, wr, experts
+
+
+def _check_topk(probs, idx, k, tol=1e-5):
+    """idx [T, k] is a valid choice of the k most probable experts: distinct,
+    and none less probable than the k-th largest probability by more than tol
+    (equal probabilities within rounding may be taken in either order)."""
+    T, E = probs.shape
+    assert idx.shape == (T, k)
+    assert np.all((idx >= 0) & (idx < E))
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1]) if k > 1 else True
+    kth = -np.sort(-probs, axis=1)[:, k - 1]
+    chosen = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
+    assert np.all(chosen >= kth[:, None] - tol), np.max(kth[:, None] - chosen)
+    # in probability order (slot 0 the most probable), up to ties
+    assert np.all(chosen[:, :-1] >= chosen[:, 1:] - tol)
+
+
+def test_moe_interleave(G):
+    grok, U, torch = G
+    g = gi.rng(77)
+    d, F = 40, 24
+    wg, wv = gi.int8_uniform(g, (d, F)), gi.int8_uniform(g, (d, F))
+    sg, sv = g.uniform(0.5, 1.5, F).astype(np.float32), g.uniform(0.5, 1.5, F).astype(np.float32)
+    wgv, sgv = grok.grok_moe_interleave(U.dev(wg), U.dev(sg), U.dev(wv), U.dev(sv))
+    torch.cuda.synchronize()
+    ref = np.empty((d, 2 * F), np.int8)
+    refs = np.empty(2 * F, np.float32)
+    for q in range(F // 4):
+        ref[:, 8 * q:8 * q + 4], ref[:, 8 * q + 4:8 * q + 8] = wg[:, 4 * q:4 * q + 4], wv[:, 4 * q:4 * q + 4]
+        refs[8 * q:8 * q + 4], refs[8 * q + 4:8 * q + 8] = sg[4 * q:4 * q + 4], sv[4 * q:4 * q + 4]
+    assert np.array_equal(wgv.cpu().numpy(), ref)
+    assert np.array_equal(sgv.cpu().numpy(), refs)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(37, 6144, 8, 2), (1, 64, 3, 2), (300, 200, 8, 4), (9, 8, 1, 1)])
+def test_moe_route(G, T, d, E, k):
+    grok, U, torch = G
+    g = gi.rng(T + d)
+    nb = gi.normal_bf16(g, (T, d))
+    wr = (gi.normal_f32(g, (d, E)) * np.float32(1.5 / math.sqrt(d))).astype(np.float32)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    grok.grok_moe_route(U.dev_bf16(nb), U.dev(wr), idx, gates)
+    torch.cuda.synchronize()
+    probs, _, _ = orc.moe_route(orc.bf16_bits_to_f64(nb), wr, k)
+    gi_ = idx.cpu().numpy()
+    _check_topk(probs, gi_, k)
+    U.assert_f32_close(gates.cpu().numpy(), np.take_along_axis(probs, gi_.astype(np.int64), axis=1), "gates")
+
+
+def _skewed_router(g, d, E, x_bits):
+    """Router weights under which most rows pick expert 0 first and none picks
+    expert E-1: both columns follow a direction u that every row of x shares."""
+    x = orc.bf16_bits_to_f64(x_bits)
+    u = np.sign(g.standard_normal(d))
+    x = x + u                                          # every row leans along u
+    wr = (gi.normal_f32(g, (d, E)) * np.float32(1.5 / math.sqrt(d))).astype(np.float32)
+    wr[:, 0] += (u * 5.0 / d).astype(np.float32)       # logit about +3.5 for expert 0
+    wr[:, E - 1] -= (u * 20.0 / d).astype(np.float32)  # about -14 for expert E-1
+    return gi.f32_to_bf16_bits(x.astype(np.float32)), wr
+
+
+@pytest.mark.parametrize("T,d,F,E,k,case", [
+    (600, 256, 384, 4, 2, "plain"),      # ~300 rows per expert: two row tiles, ragged
+    (333, 200, 72, 8, 2, "distinct"),    # K and N tails in both products, per-channel scales
+    (1, 64, 32, 8, 2, "plain"),          # a single token
+    (130, 128, 64, 3, 2, "plain"),       # three experts
+    (200, 64, 48, 4, 4, "distinct"),     # every expert chosen by every token
+    (520, 128, 96, 8, 2, "skewed"),      # one large group, one empty expert
+])
+def test_moe_ffn(G, T, d, F, E, k, case):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    p = gi.make_moe_inputs(1, T, d, F, E, seed=900 + T, distinct_scales=(case == "distinct"),
+                           scale_up=1.0 / (127 * math.sqrt(d) * 0.58), scale_down=1.0 / (127 * math.sqrt(F) * 0.58 * 0.4))
+    p["x"] = p["x"].reshape(T, d)
+    if case == "skewed":
+        p["x"], p["w_router"] = _skewed_router(gi.rng(5), d, E, p["x"])
+    x, wr, experts = _moe_dev(U, p)
+    step = pipe.MoeStep(x, wr, experts, k=k)
+    y = step()
+    torch.cuda.synchronize()
+    idx = step.idx.cpu().numpy().astype(np.int64)
+    x64 = orc.bf16_bits_to_f64(p["x"])
+    n = orc.rmsnorm(x64, None, 1e-5, out="bf16")
+    probs, _, _ = orc.moe_route(n, p["w_router"], k)
+    # The router's own arithmetic is checked on identical inputs above; here its
+    # input is the GPU's normalised rows, which may differ from the oracle's by
+    # one bf16 rounding in a few elements (fp32 vs fp64 norm), moving a logit
+    # by up to about |w_r| * 2^-8: the probabilities get a looser bound.
+    _check_topk(probs, idx, k, tol=MOE_GATE_TOL)
+    gerr = np.abs(step.gates.cpu().numpy() - np.take_along_axis(probs, idx, axis=1)).max()
+    assert gerr <= MOE_GATE_TOL, gerr
+    if case == "skewed":
+        counts = np.bincount(idx.ravel(), minlength=E)
+        assert counts[0] > T // 2 and counts[E - 1] == 0, counts
+    ref, _, _ = orc.moe_sublayer(x64, p["w_router"], p["experts"], 1e-5, k, idx=idx)
+    # y = x + n(mix): the relative part of the bound belongs to the larger of |y|
+    # and the normalised summand, here ref - x (exact up to ref's rounding)
+    nm = ref - x64
+    assert np.abs(U.host(y) - x64).max() > 0.5  # the expert branch contributed
+    err = U.assert_bf16_close(U.host(y), ref, f"moe {case}", magnitude=np.maximum(np.abs(ref), np.abs(nm)))
+    print(f"moe T={T} d={d} F={F} E={E} k={k} {case}: max abs err {err:.2e}, rel L2 {U.rel_l2(U.host(y), ref):.2e}")
+
+
+def test_moe_ffn_repeat_and_empty(G):
+    """Two calls on the same buffers give the same bits (the plan is rebuilt
+    every call, nothing carries over); T = 0 is a no-op."""
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    p = gi.make_moe_inputs(1, 100, 128, 64, 8, seed=31)
+    x, wr, experts = _moe_dev(U, p)
+    step = pipe.MoeStep(x.reshape(100, 128), wr, experts)
+    a = U.bits(step()).copy()
+    b = U.bits(step())
+    assert np.array_equal(a, b)
+    e = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    grok.grok_moe_ffn(e, wr, step.wgv, step.sgv, step.w1, step.s1, torch.empty_like(e), ws)

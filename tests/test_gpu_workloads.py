@@ -229,3 +229,45 @@ def test_prefill_chunk_b4_t512_sampled(G):
                                   for h in range(Hq)])
             errs.append(U.assert_bf16_close(out[b, t], ref, f"chunk b={b} (offset {o}) t={t}"))
     print(f"chunk sampled rows, max abs err {max(errs):.2e}")
+
+
+def test_moe_b4_t2048_sampled(G):
+    """The MoE FFN sub-layer at its full size (8192 token rows, d 6144, F 32768,
+    8 experts, top-2): the routing of every row is a valid top-2 of the oracle's
+    probabilities with the oracle's gates, and sampled rows match the oracle
+    run on those rows with the same expert choice."""
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS["moe_b4_t2048"]
+    p = gi.make_workload(w.name)
+    T, d = w.B * w.T, w.d_model
+    xb = p["x"].reshape(T, d)
+    x = U.dev_bf16(xb)
+    experts = [tuple(U.dev(a) for a in ex) for ex in p["experts"]]
+    step = pipe.MoeStep(x, U.dev(p["w_router"]), experts, k=w.top_k)
+    del experts
+    y = U.host(step())
+    torch.cuda.synchronize()
+    print("moe: GPU step done", flush=True)
+    idx = step.idx.cpu().numpy().astype(np.int64)
+    gates = step.gates.cpu().numpy()
+    x64 = orc.bf16_bits_to_f64(xb)
+    n = orc.rmsnorm(x64, None, w.eps, out="bf16")
+    probs, _, _ = orc.moe_route(n, p["w_router"], w.top_k)
+    kth = -np.sort(-probs, axis=1)[:, w.top_k - 1]
+    chosen = np.take_along_axis(probs, idx, axis=1)
+    assert np.all((idx >= 0) & (idx < w.n_experts)) and np.all(idx[:, 0] != idx[:, 1])
+    # the GPU routes its own normalised rows, which may differ from the oracle's
+    # by one bf16 rounding in a few elements: probabilities agree to ~1e-4
+    assert np.all(chosen >= kth[:, None] - 1e-3)
+    gerr = np.abs(gates - chosen).max()
+    assert gerr <= 1e-3, gerr
+    print(f"moe: max gate error {gerr:.2e}", flush=True)
+    counts = np.bincount(idx.ravel(), minlength=w.n_experts)
+    print(f"moe: routing valid, rows per expert {counts.tolist()}", flush=True)
+    rows = np.array([0, T - 1] + list(gi.rng(4444).integers(1, T - 1, 2)))
+    ref, _, _ = orc.moe_sublayer(x64[rows], p["w_router"], p["experts"], w.eps, w.top_k, idx=idx[rows])
+    # y = x + n(mix): the relative part of the bound belongs to the larger of
+    # |y| and the normalised summand, here ref - x (exact up to ref's rounding)
+    nm = ref - x64[rows]
+    err = U.assert_bf16_close(y[rows], ref, "moe sampled rows", magnitude=np.maximum(np.abs(ref), np.abs(nm)))
+    print(f"moe sampled rows {rows.tolist()}: max abs err {err:.2e}, rel L2 {U.rel_l2(y[rows], ref):.2e}")
