@@ -12,7 +12,10 @@ Sources (the Grok-1 walkthrough pages; section numbers are the pages' own):
   (yingwang.github.io/grok-1/06-model-3/): §6.3/§6.3.1 sandwich norm,
   §6.4.2 causal x padding mask, §6.6 KV memory.
 * [ch3] "Configuration and hyperparameters" (yingwang.github.io/grok-1/03-config/):
-  §3.3 / §3.3.2 attention constants.
+  §3.3 / §3.3.2 attention constants, §3.5 the router.
+* [ch2] "Overall architecture" (yingwang.github.io/grok-1/02-architecture/):
+  §2.2 data flow of a layer, §2.5.1 unnormalised top-2 gates.
+* [ch6] §6.2 the gated FFN of one expert (``jax.nn.gelu`` on the gate).
 
 Everything is float64 unless a step's precision is fixed by the pages (the
 RoPE phase is float32 there, [ch4] §4.3.1). Results are rounded to the output
