@@ -268,9 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       // softcap + shifted exp -> P (bf16) in the B-operand layout of P.V:
       // p = exp2(k2 / (1 + exp2(k1*s))) = exp2(rcp((1 + e) * (1/k2))).
       const bool diag = kMask && hk0 + 31 > wmin;
-      bf16x8 pf[kRB];
-#pragma unroll
-      for (int i = 0; i < kRB; ++i) {
+      auto softmax_rows = [&](int i) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -289,24 +287,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
         }
         const u32x4 w = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                          cvt_pk_bf16(p[6], p[7])};
-        pf[i] = __builtin_bit_cast(bf16x8, w);
         // Row sum of the bf16-rounded weights that the P.V product uses (so the
         // normalised weights of a row sum to one): bf16 pair dot (1, 1).
 #pragma unroll
         for (int e = 0; e < 4; ++e) lsum[i] = add_bf16_pair(lsum[i], w[e]);
-      }
+        return __builtin_bit_cast(bf16x8, w);
+      };
       // O^T += V^T . P^T; the V^T fragment of lane l (dim 16*db + lr, keys
       // 8*lg .. 8*lg+7 of the half) comes from two transpose reads of 4 keys.
       u32x2 lo[8], hi[8];
-      read_vt_half<h * 32 * kRowBytes>(lo, hi, amb, std::make_integer_sequence<int, 8>{});
-      lds_wait<8>(lo, hi);
+      if constexpr (!kHasValid && !kOffset) {
+        // Plain prefill: the V^T reads go out first and land during the first
+        // softmax; then row block by row block, so that the P.V MFMAs of one
+        // block execute while the next block's softmax is issued.
+        read_vt_half<h * 32 * kRowBytes>(lo, hi, amb, std::make_integer_sequence<int, 8>{});
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        if (db == 4) lds_wait<0>(lo + 4, hi + 4);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[db][0], lo[db][1], hi[db][0], hi[db][1]});
+        for (int i = 0; i < kRB; ++i) {
+          const bf16x8 pfi = softmax_rows(i);
+          if (i == 0) lds_wait<0>(lo, hi), lds_wait<0>(lo + 4, hi + 4);
 #pragma unroll
-        for (int i = 0; i < kRB; ++i)
-          oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], oacc[i][db], 0, 0, 0);
+          for (int db = 0; db < 8; ++db) {
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[db][0], lo[db][1], hi[db][0], hi[db][1]});
+            oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfi, oacc[i][db], 0, 0, 0);
+          }
+        }
+      } else {
+        // With padding masks or a cache offset the register budget is tighter:
+        // all softmaxes first, then the V^T reads and the P.V product.
+        bf16x8 pf[kRB];
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) pf[i] = softmax_rows(i);
+        read_vt_half<h * 32 * kRowBytes>(lo, hi, amb, std::make_integer_sequence<int, 8>{});
+        lds_wait<8>(lo, hi);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          if (db == 4) lds_wait<0>(lo + 4, hi + 4);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[db][0], lo[db][1], hi[db][0], hi[db][1]});
+#pragma unroll
+          for (int i = 0; i < kRB; ++i)
+            oacc[i][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[i], oacc[i][db], 0, 0, 0);
+        }
       }
     };
     half(std::integral_constant<int, 0>{});

@@ -778,3 +778,56 @@ def test_moe_ffn_repeat_and_empty(G):
     e = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
     grok.grok_moe_ffn(e, wr, step.wgv, step.sgv, step.w1, step.s1, torch.empty_like(e), ws)
+
+
+def test_slot_insertion_into_a_batched_cache_then_batched_decode(G):
+    """Continuous batching through the C ABI: a new prompt is prefilled into one
+    free slot of a batched cache (append + chunk attention on that slot's view,
+    offset 0), leaving the other slots' bytes untouched; then one batched decode
+    step runs over every slot at its own position. The inserted slot's prefill
+    equals the cache-free prefill bit for bit, and every decode row matches the
+    oracle's decode step of that sequence."""
+    grok, U, torch = G
+    g = gi.rng(91)
+    B, Tmax, Hq, Hkv, D, T = 4, 256, 12, 2, 128, 100
+    mult, slot = 0.2, 2
+    kc0, vc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D)), gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    kc, vc = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    qp, kp, vp = gi.normal_bf16(g, (1, T, Hq, D)), gi.normal_bf16(g, (1, T, Hkv, D)), gi.normal_bf16(g, (1, T, Hkv, D))
+    q = U.dev_bf16(qp)
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ks, vs = kc[slot:slot + 1], vc[slot:slot + 1]          # views of one slot (batch-major: contiguous)
+    grok.grok_kv_append(ks, vs, U.dev_bf16(kp), U.dev_bf16(vp), zero, q_inout=q, status=status)
+    out = torch.empty((1, T, Hq * D), dtype=torch.bfloat16, device="cuda")
+    grok.grok_attn_prefill_chunk(q, ks, vs, zero, out, mult, status=status)
+    # the same prompt without a cache: RoPE q and k at 0..T-1, causal prefill
+    qr, kr = U.dev_bf16(qp), U.dev_bf16(kp)
+    grok.grok_rope(qr)
+    grok.grok_rope(kr)
+    ref = torch.empty_like(out)
+    grok.grok_attn_prefill(qr, kr, U.dev_bf16(vp), ref, mult)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    np.testing.assert_array_equal(U.bits(out), U.bits(ref))
+    kcb, vcb = U.bits(kc), U.bits(vc)
+    for b in range(B):
+        if b != slot:
+            np.testing.assert_array_equal(kcb[b], kc0[b])
+            np.testing.assert_array_equal(vcb[b], vc0[b])
+    np.testing.assert_array_equal(kcb[slot, T:], kc0[slot, T:])
+    np.testing.assert_array_equal(kcb[slot, :T], U.bits(kr)[0])
+    # one batched decode step: every slot continues at its own position
+    step = np.array([50, 120, T, 30], np.int32)
+    qn, kn, vn = (gi.normal_bf16(g, (B, 1, Hq, D)), gi.normal_bf16(g, (B, 1, Hkv, D)),
+                  gi.normal_bf16(g, (B, 1, Hkv, D)))
+    dout = torch.empty((B, 1, Hq * D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+    kc_before, vc_before = orc.bf16_bits_to_f64(U.bits(kc)), orc.bf16_bits_to_f64(U.bits(vc))
+    grok.grok_attn_decode_append(U.dev_bf16(qn), U.dev_bf16(kn), U.dev_bf16(vn), kc, vc, U.dev(step), dout, ws,
+                                 mult, status=status)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    ref_out, _, _, _ = orc.decode_step(kc_before, vc_before, orc.bf16_bits_to_f64(qn), orc.bf16_bits_to_f64(kn),
+                                       orc.bf16_bits_to_f64(vn), step, mult)
+    U.assert_bf16_close(U.host(dout), ref_out, "batched decode after slot insertion")
