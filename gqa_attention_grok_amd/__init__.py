@@ -24,7 +24,7 @@ __all__ = [
     "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
     "grok_attn_decode_workspace_bytes", "grok_moe_workspace_bytes", "grok_moe_interleave",
-    "grok_moe_route", "grok_moe_ffn",
+    "grok_moe_route", "grok_moe_ffn", "grok_prefill_qkv_workspace_bytes", "grok_prefill_qkv",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrokattn.so")
@@ -59,6 +59,9 @@ _PROTOS = {
     "grok_attn_decode_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i,
                                      _f, _f, _f, _p]),
     "grok_moe_workspace_bytes": (_sz, [_i64, _i, _i, _i, _i]),
+    "grok_prefill_qkv_workspace_bytes": (_sz, [_i, _i]),
+    "grok_prefill_qkv": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i,
+                              _i, _f, _p]),
     "grok_moe_interleave": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _p]),
     "grok_moe_route": (_i, [_p, _p, _p, _p, _i64, _i, _i, _i, _p]),
     "grok_moe_ffn": (_i, [_p, _p, _i, _i, _p, _p, _p, _p, _i64, _i, _i, _f, _p, _p, _p, _sz, _p, _p]),
@@ -410,3 +413,37 @@ def grok_moe_ffn(x, w_router, wgv, sgv, w1, s1, out, workspace, k=2, eps=1e-5, i
                             workspace.numel() * workspace.element_size(), _ptr(out), _stream(x)),
            "grok_moe_ffn")
     return out
+
+
+def grok_prefill_qkv_workspace_bytes(Tmax, D=128) -> int:
+    return lib.grok_prefill_qkv_workspace_bytes(Tmax, D)
+
+
+def grok_prefill_qkv(x, wq, sq, wk, sk, wv, sv, q_out, k_cache, v_cache, workspace, step=None, new_step=None,
+                     status=None, rope_base=10000.0):
+    """T rows per sequence in one launch: q_out = rope(x Wq) at step[b] + t; the
+    cache slots step[b] + t get rope(x Wk) and x Wv (step None: positions t)."""
+    _need(x, "x", torch.bfloat16, 3)
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv")):
+        _need(t, n, torch.int8, 2)
+    for t, n in ((sq, "sq"), (sk, "sk"), (sv, "sv")):
+        _need(t, n, torch.float32, 1)
+    _need(q_out, "q_out", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(workspace, "workspace")
+    _need(step, "step", torch.int32, 1)
+    _need(new_step, "new_step", torch.int32, 1)
+    _need(status, "status", torch.int32)
+    B, T, d = x.shape
+    Hq, D = q_out.shape[2], q_out.shape[3]
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(q_out.shape[:2]) != (B, T) or tuple(wq.shape) != (d, Hq * D) or tuple(wk.shape) != (d, Hkv * D) \
+            or tuple(wv.shape) != (d, Hkv * D) or k_cache.shape != v_cache.shape or k_cache.shape[0] != B:
+        raise ValueError("prefill_qkv: shapes do not match")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.grok_prefill_qkv(_ptr(x), _ptr(wq), _ptr(sq), _ptr(wk), _ptr(sk), _ptr(wv), _ptr(sv), _ptr(q_out),
+                                _ptr(k_cache), _ptr(v_cache), _ptr(step), _ptr(new_step), _ptr(status),
+                                _ptr(workspace), ws_bytes, B, T, d, Tmax, Hq, Hkv, D, rope_base, _stream(x)),
+           "grok_prefill_qkv")
+    return q_out

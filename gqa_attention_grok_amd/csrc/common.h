@@ -104,6 +104,21 @@ hipError_t launch_moe_ffn(const void *x, const float *w_router, int E, int k, co
                           const float *const *sgv, const int8_t *const *w1, const float *const *s1, int64_t T,
                           int d, int F, float eps, int32_t *idx, float *gates, void *workspace, void *out,
                           hipStream_t s);
+// Fused Q/K/V projection of T rows per sequence (linear_int8.hip): one head
+// (128 channels) per column tile, RoPE and the cache write in the epilogue.
+struct PrefillQkvArgs {
+  bf16_t *out[3];         // q_out [B,T,Hq,128], k_cache, v_cache [B,Tmax,Hkv,128]
+  const int8_t *w[3];     // Wq [d, Hq*128], Wk, Wv [d, Hkv*128]
+  const float *s[3];
+  const int32_t *step;    // [B] first position of each sequence, or NULL (0)
+  int32_t *new_step;      // [B] or NULL
+  int32_t *status;        // or NULL
+  const float *rtab;      // [Tmax][128]: cos of pairs 0..63, then sin
+  int B, T, Tmax, Hq, Hkv;
+};
+size_t prefill_qkv_workspace_bytes(int Tmax);
+hipError_t launch_prefill_qkv(const void *x, const PrefillQkvArgs &qa, void *workspace, int d, float rope_base,
+                              hipStream_t s);
 // Few-row int8 Linear on packed weights (layout in linear_int8_gemv.hip).
 size_t gemv_packed_bytes(int K, int N);
 hipError_t launch_linear_int8_pack(const int8_t *w, int8_t *wp, int K, int N, hipStream_t s);

@@ -371,4 +371,55 @@ int grok_moe_ffn(const void *x, const float *w_router, int E, int k, const int8_
                     "moe_ffn");
 }
 
+size_t grok_prefill_qkv_workspace_bytes(int Tmax, int D) {
+  if (Tmax < 1 || D != 128) return 0;
+  return grok::prefill_qkv_workspace_bytes(Tmax);
+}
+
+int grok_prefill_qkv(const void *x, const int8_t *wq, const float *sq, const int8_t *wk, const float *sk,
+                     const int8_t *wv, const float *sv, void *q_out, void *k_cache, void *v_cache,
+                     const int32_t *step, int32_t *new_step, int32_t *status, void *workspace, size_t ws_bytes,
+                     int B, int T, int d, int Tmax, int Hq, int Hkv, int D, float rope_base,
+                     hipStream_t stream) {
+  if (B < 1 || T < 1 || d < 8 || d % 8 || Tmax < 1 || Hq < 1 || Hkv < 1)
+    return fail(GROK_EINVAL, "prefill_qkv: bad shape B=%d T=%d d=%d Tmax=%d Hq=%d Hkv=%d", B, T, d, Tmax, Hq, Hkv);
+  if (D != 128) return fail(GROK_EINVAL, "prefill_qkv: head size must be 128 (D=%d)", D);
+  if (T > Tmax) return fail(GROK_EINVAL, "prefill_qkv: T=%d exceeds Tmax=%d", T, Tmax);
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return fail(GROK_EINVAL, "prefill_qkv: bad rope_base");
+  if ((static_cast<int64_t>(B) * T + 255) / 256 > 65535 || Hq + 2 * Hkv > 65535 ||
+      static_cast<int64_t>(Tmax) * 128 > 0x7fffffff)
+    return fail(GROK_EINVAL, "prefill_qkv: sizes too large");
+  if (!x || !wq || !sq || !wk || !sk || !wv || !sv || !q_out || !k_cache || !v_cache || !workspace)
+    return fail(GROK_EINVAL, "prefill_qkv: null pointer");
+  if (new_step && new_step == step) return fail(GROK_EINVAL, "prefill_qkv: new_step must not alias step");
+  const uintptr_t a16 = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(sq) |
+                        reinterpret_cast<uintptr_t>(sk) | reinterpret_cast<uintptr_t>(sv) |
+                        reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(k_cache) |
+                        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(workspace);
+  const uintptr_t a8 = reinterpret_cast<uintptr_t>(wq) | reinterpret_cast<uintptr_t>(wk) |
+                       reinterpret_cast<uintptr_t>(wv);
+  if (a16 % 16 || a8 % 8) return fail(GROK_EINVAL, "prefill_qkv: misaligned pointer");
+  const size_t need = grok::prefill_qkv_workspace_bytes(Tmax);
+  if (ws_bytes < need) return fail(GROK_ENOMEM, "prefill_qkv: workspace %zu bytes < %zu needed", ws_bytes, need);
+  grok::PrefillQkvArgs qa = {};
+  qa.out[0] = static_cast<grok::bf16_t *>(q_out);
+  qa.out[1] = static_cast<grok::bf16_t *>(k_cache);
+  qa.out[2] = static_cast<grok::bf16_t *>(v_cache);
+  qa.w[0] = wq;
+  qa.w[1] = wk;
+  qa.w[2] = wv;
+  qa.s[0] = sq;
+  qa.s[1] = sk;
+  qa.s[2] = sv;
+  qa.step = step;
+  qa.new_step = new_step;
+  qa.status = status;
+  qa.B = B;
+  qa.T = T;
+  qa.Tmax = Tmax;
+  qa.Hq = Hq;
+  qa.Hkv = Hkv;
+  return hip_status(grok::launch_prefill_qkv(x, qa, workspace, d, rope_base, stream), "prefill_qkv");
+}
+
 }  // extern "C"

@@ -104,10 +104,16 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 // kGeGLU: the weight columns hold gate and value channels interleaved by four
 // (columns 8q..8q+3 = gate channels 4q..4q+3, 8q+4..8q+7 = value channels),
 // and the epilogue writes h = gelu(gate) * value into y [M, N/2].
-template <bool kGrouped, bool kGather, bool kGeGLU>
+// kQkv: the fused Q/K/V projection (PrefillQkvArgs): column tile c is head c of Q,
+// then the heads of K, then of V (128 channels each, D = 128 = kBN); the
+// epilogue rounds the projection to bf16 as a separate projection would, then
+// rotates Q and K at their positions (the two halves of a head sit in waves w
+// and w ^ 1 at the same register and lane: one exchange through LDS) and
+// writes q to its buffer and k, v to their cache slots.
+template <bool kGrouped, bool kGather, bool kGeGLU, bool kQkv = false>
 __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
     const bf16_t *__restrict__ x, const int8_t *__restrict__ w_in, const float *__restrict__ scales_in,
-    bf16_t *__restrict__ y, int64_t M, int K, int N, GroupArgs ga) {
+    bf16_t *__restrict__ y, int64_t M, int K, int N, GroupArgs ga, PrefillQkvArgs qa = {}) {
   __shared__ __attribute__((aligned(1024))) unsigned char Xs[3][kXTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char Wt[2][kTileB];
 
@@ -116,10 +122,20 @@ __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lr = lane % 16, lg = lane / 16;
   const int wn = wave % 2, wm = wave / 2;
-  const int n0 = blockIdx.x * kBN;
+  int n0 = blockIdx.x * kBN;
   int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   const int8_t *w = w_in;
   const float *scales = scales_in;
+  int mat = 0, head = 0;
+  if constexpr (kQkv) {
+    const int c = blockIdx.x;
+    mat = c < qa.Hq ? 0 : (c < qa.Hq + qa.Hkv ? 1 : 2);
+    head = c - (mat == 0 ? 0 : (mat == 1 ? qa.Hq : qa.Hq + qa.Hkv));
+    w = qa.w[mat];
+    scales = qa.s[mat];
+    N = (mat == 0 ? qa.Hq : qa.Hkv) * kBN;
+    n0 = head * kBN;
+  }
   if constexpr (kGrouped) {
     // this tile's group: walk the groups' tile counts (uniform, scalar loads)
     int ty = blockIdx.y, e = -1;
@@ -308,6 +324,84 @@ __global__ __launch_bounds__(kThreads, 1) void linear_int8_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   // Epilogue: lane holds Y^T[n = nbase + 4*lg + v, m = mbase + lr], v = 0..3.
+  if constexpr (kQkv) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {  // per sequence: new_step, status
+      for (int bb = tid; bb < qa.B; bb += kThreads) {
+        const int s0 = qa.step ? qa.step[bb] : 0;
+        const bool ok = s0 >= 0 && s0 <= qa.Tmax - qa.T;
+        if (qa.new_step) qa.new_step[bb] = ok ? s0 + qa.T : s0;
+        if (!ok && qa.status) *qa.status = GROK_ERANGE;
+      }
+    }
+    // the projection handed on in bf16, packed in pairs: r[nb][mb][h] holds v = 2h, 2h+1
+    uint32_t r[4][4][2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x4 sc = *reinterpret_cast<const f32x4 *>(scales + n0 + 64 * wn + 16 * nb + 4 * lg);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const f32x4 v = acc[nb][mb];
+        r[nb][mb][0] = cvt_pk_bf16(v[0] * sc[0], v[1] * sc[1]);
+        r[nb][mb][1] = cvt_pk_bf16(v[2] * sc[2], v[3] * sc[3]);
+      }
+    }
+    uint32_t pr[4][4][2];  // the partner half of the head (channel d +- 64)
+    if (mat < 2) {
+      // every wave is past its last LDS read (loop barrier) and its own tile
+      // loads (wait above); after this barrier no load still targets Xs
+      __syncthreads();
+      uint32_t *xch = reinterpret_cast<uint32_t *>(&Xs[0][0]);  // [8 waves][32][64 lanes]
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) xch[(wave * 32 + (nb * 4 + mb) * 2 + h) * kWave + lane] = r[nb][mb][h];
+      __syncthreads();
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) pr[nb][mb][h] = xch[((wave ^ 1) * 32 + (nb * 4 + mb) * 2 + h) * kWave + lane];
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int64_t m = m0 + 64 * wm + 16 * mb + lr;
+      if (m >= M) continue;
+      const int bq = static_cast<int>(m / qa.T), t = static_cast<int>(m % qa.T);
+      const int s0 = qa.step ? qa.step[bq] : 0;
+      if (s0 < 0 || s0 > qa.Tmax - qa.T) continue;  // sequence outside the cache: nothing is written
+      const int pos = s0 + t;
+      bf16_t *dst = mat == 0 ? qa.out[0] + (m * qa.Hq + head) * kBN
+                             : qa.out[mat] + ((static_cast<int64_t>(bq) * qa.Tmax + pos) * qa.Hkv + head) * kBN;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int d = 64 * wn + 16 * nb + 4 * lg;
+        u32x2 o = {r[nb][mb][0], r[nb][mb][1]};
+        if (mat < 2) {
+          const int i = 16 * nb + 4 * lg;  // pair index of v = 0
+          const f32x4 cs = *reinterpret_cast<const f32x4 *>(qa.rtab + pos * 128 + i);
+          const f32x4 sn = *reinterpret_cast<const f32x4 *>(qa.rtab + pos * 128 + 64 + i);
+          float ov[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t mine = r[nb][mb][v >> 1], other = pr[nb][mb][v >> 1];
+            const float xm = (v & 1) ? hi_bf16(mine) : lo_bf16(mine);
+            const float xo = (v & 1) ? hi_bf16(other) : lo_bf16(other);
+            float o1, o2;
+            if (wn == 0)
+              rope_rotate(xm, xo, cs[v], sn[v], o1, o2), ov[v] = o1;
+            else
+              rope_rotate(xo, xm, cs[v], sn[v], o1, o2), ov[v] = o2;
+          }
+          o = u32x2{cvt_pk_bf16(ov[0], ov[1]), cvt_pk_bf16(ov[2], ov[3])};
+        }
+        *reinterpret_cast<u32x2 *>(dst + d) = o;
+      }
+    }
+    return;
+  }
   if constexpr (kGeGLU) {
     // lanes lg and lg ^ 1 hold the gate and the value columns of the same 4
     // channels: the even one combines and stores them. Both projections are
@@ -394,6 +488,40 @@ hipError_t launch_linear_int8_grouped(const void *x, const int32_t *rows, const 
   else
     hipLaunchKernelGGL((linear_int8_kernel<true, false, false>), grid, dim3(kThreads), 0, s, xb, w[0], scales[0],
                        yb, M_total, K, N, ga);
+  return hipGetLastError();
+}
+
+namespace {
+
+// cos / sin of every (position, pair) of a head of 128, from the pinned RoPE
+// helpers, so that the fused epilogue rotates with the bits of the RoPE kernels.
+__global__ __launch_bounds__(64) void rope_table_kernel(float *tab, RopeFreqs f) {
+  const int pos = blockIdx.x, i = threadIdx.x;
+  float sn, cs;
+  rope_phase(pos, f.inv[i], sn, cs);
+  tab[pos * 128 + i] = cs;
+  tab[pos * 128 + 64 + i] = sn;
+}
+
+}  // namespace
+
+size_t prefill_qkv_workspace_bytes(int Tmax) { return static_cast<size_t>(Tmax) * 128 * sizeof(float); }
+
+hipError_t launch_prefill_qkv(const void *x, const PrefillQkvArgs &qa_in, void *workspace, int d, float rope_base,
+                              hipStream_t s) {
+  RopeFreqs f;
+  rope_build_freqs(kBN, rope_base, &f);
+  PrefillQkvArgs qa = qa_in;
+  qa.rtab = static_cast<const float *>(workspace);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(qa.Tmax), dim3(64), 0, s, static_cast<float *>(workspace), f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t M = static_cast<int64_t>(qa.B) * qa.T;
+  const int64_t gm = (M + kBM - 1) / kBM;
+  if (gm > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid(qa.Hq + 2 * qa.Hkv, static_cast<unsigned>(gm));
+  hipLaunchKernelGGL((linear_int8_kernel<false, false, false, true>), grid, dim3(kThreads), 0, s,
+                     static_cast<const bf16_t *>(x), qa.w[0], qa.s[0], qa.out[0], M, d, qa.Hq * kBN, GroupArgs{}, qa);
   return hipGetLastError();
 }
 

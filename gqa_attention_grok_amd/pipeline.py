@@ -32,7 +32,7 @@ from . import (grok_attn_decode, grok_attn_decode_append, grok_attn_decode_works
                grok_attn_prefill, grok_attn_prefill_chunk,
                grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
                grok_linear_int8_pack, grok_moe_ffn, grok_moe_interleave, grok_moe_workspace_bytes,
-               grok_rmsnorm, grok_rope)
+               grok_prefill_qkv, grok_prefill_qkv_workspace_bytes, grok_rmsnorm, grok_rope)
 
 
 def capture(step) -> "torch.cuda.CUDAGraph":
@@ -139,10 +139,14 @@ class ChunkStep:
 
 
 class SublayerStep:
-    """Attention sub-layer with unit-scale norms and int8 projections."""
+    """Attention sub-layer with unit-scale norms and int8 projections.
+    fused=True runs the Q/K/V projections, RoPE of q and k and the writes of
+    q, k, v as one launch (grok_prefill_qkv); fused=False runs three
+    projections and two RoPE passes."""
 
     def __init__(self, x, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D, attn_mult, softcap=30.0,
-                 eps=1e-5, rope_base=10000.0, key_valid=None):
+                 eps=1e-5, rope_base=10000.0, key_valid=None, fused=True):
+        self.fused = fused
         self.x = x
         self.w = (wq, sq, wk, sk, wv, sv, wo, so)
         self.Hq, self.Hkv, self.D = Hq, Hkv, D
@@ -158,15 +162,20 @@ class SublayerStep:
         self.attn = torch.empty((B, T, Hq * D), dtype=bf, device=dev)
         self.o = torch.empty((B, T, d), dtype=bf, device=dev)
         self.y = torch.empty((B, T, d), dtype=bf, device=dev)
+        self.ws = torch.empty(grok_prefill_qkv_workspace_bytes(T, D), dtype=torch.uint8, device=dev)
 
     def __call__(self):
         wq, sq, wk, sk, wv, sv, wo, so = self.w
         grok_rmsnorm(self.x, self.n, eps=self.eps)
-        grok_linear_int8(self.n, wq, sq, self.q)
-        grok_linear_int8(self.n, wk, sk, self.k)
-        grok_linear_int8(self.n, wv, sv, self.v)
-        grok_rope(self.q, None, self.rope_base)
-        grok_rope(self.k, None, self.rope_base)
+        if self.fused:
+            grok_prefill_qkv(self.n, wq, sq, wk, sk, wv, sv, self.q, self.k, self.v, self.ws,
+                             rope_base=self.rope_base)
+        else:
+            grok_linear_int8(self.n, wq, sq, self.q)
+            grok_linear_int8(self.n, wk, sk, self.k)
+            grok_linear_int8(self.n, wv, sv, self.v)
+            grok_rope(self.q, None, self.rope_base)
+            grok_rope(self.k, None, self.rope_base)
         grok_attn_prefill(self.q, self.k, self.v, self.attn, self.attn_mult, self.softcap,
                           key_valid=self.key_valid)
         grok_linear_int8(self.attn, wo, so, self.o)

@@ -297,6 +297,36 @@ GROK_API int grok_attn_decode_append(const void *q, const void *k_new, const voi
 GROK_API size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D);
 
 /*
+ * Front half of the attention sub-layer for T rows per sequence, in one launch
+ * ([ch4] §4.1 int8 Linear, §4.5.1 projections, §4.3.1 RoPE, §4.4 RoPE before
+ * the cache write): for each sequence b with s = step[b] (0 if step is NULL)
+ * and row t,
+ *   q_out[b, t]          = rope(x[b, t] @ (Wq * sq), s + t)
+ *   k_cache[b, s + t]    = rope(x[b, t] @ (Wk * sk), s + t)
+ *   v_cache[b, s + t]    = x[b, t] @ (Wv * sv)
+ * with the numerics (and the bits) of three grok_linear_int8 calls followed
+ * by grok_kv_append: each projection is rounded to bf16, then rotated. With
+ * step NULL and Tmax == T the "cache" is simply the [B, T, Hkv, 128] K and V
+ * of a prompt. new_step[b] = s + T if new_step is not NULL.
+ *   x [B, T, d] bf16 (the normalised rows); wq [d, Hq*128], wk, wv
+ *   [d, Hkv*128] int8; sq, sk, sv fp32 channel scales; q_out [B, T, Hq, 128];
+ *   caches [B, Tmax, Hkv, 128] bf16; step [B] int32 device or NULL;
+ *   workspace: device, grok_prefill_qkv_workspace_bytes(Tmax, 128) bytes (a
+ *   cos/sin table of every cache position, rebuilt by each call).
+ * A sequence with s < 0 or s + T > Tmax gets no writes at all (q_out rows
+ * untouched), new_step[b] = s, and GROK_ERANGE is stored to *status.
+ * Errors: EINVAL for NULL pointers, sizes < 1, D != 128, T > Tmax, d not a
+ * multiple of 8, a bad rope_base, new_step == step, or a misaligned pointer
+ * (16 bytes; the weights 8); ENOMEM if ws_bytes is too small.
+ */
+GROK_API size_t grok_prefill_qkv_workspace_bytes(int Tmax, int D);
+GROK_API int grok_prefill_qkv(const void *x, const int8_t *wq, const float *sq, const int8_t *wk,
+                              const float *sk, const int8_t *wv, const float *sv, void *q_out,
+                              void *k_cache, void *v_cache, const int32_t *step, int32_t *new_step,
+                              int32_t *status, void *workspace, size_t ws_bytes, int B, int T, int d,
+                              int Tmax, int Hq, int Hkv, int D, float rope_base, hipStream_t stream);
+
+/*
  * MoE FFN sub-layer: the FFN half of a decoder layer ([ch6] §6.3.1 sandwich
  * norm; [ch2] §2.2 data flow), for T token rows:
  *   n     = rmsnorm(x)                          (unit scale, bf16)

@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 20, syms
+    assert len(syms) == 22, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -300,3 +300,25 @@ def test_moe_validation_and_workspace(lib):
     assert inter(d=0) == EINVAL
     assert inter(sg=ctypes.c_void_p(0x10004)) == EINVAL
     assert inter(sg=None) == EINVAL
+
+
+def test_prefill_qkv_validation(lib):
+    wsb = lambda Tmax, D: _c(lib, "grok_prefill_qkv_workspace_bytes", i(Tmax), i(D), restype=ctypes.c_size_t)
+    assert wsb(8192, 128) == 8192 * 128 * 4       # one cos/sin row of 64 + 64 floats per position
+    assert wsb(8192, 64) == 0 and wsb(0, 128) == 0
+
+    def call(B=2, T=100, d=256, Tmax=512, Hq=6, Hkv=2, D=128, base=1e4, x=FAKE, step=FAKE,
+             new_step=ctypes.c_void_p(0x20000), ws_bytes=1 << 30, q=FAKE, wq=FAKE):
+        return _c(lib, "grok_prefill_qkv", x, wq, FAKE, FAKE, FAKE, FAKE, FAKE, q, FAKE, FAKE, step, new_step,
+                  None, FAKE, ctypes.c_size_t(ws_bytes), i(B), i(T), i(d), i(Tmax), i(Hq), i(Hkv), i(D), fl(base),
+                  None)
+    assert call(D=64) == EINVAL
+    assert call(T=600) == EINVAL and "exceeds Tmax" in _err(lib)
+    assert call(d=250) == EINVAL
+    assert call(base=-1.0) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(new_step=FAKE) == EINVAL                   # aliases step
+    assert call(q=ctypes.c_void_p(0x10008)) == EINVAL      # 16-byte alignment
+    assert call(wq=ctypes.c_void_p(0x10004)) == EINVAL     # weights: 8 bytes
+    assert call(ws_bytes=16) == ENOMEM
+    assert call(B=0) == EINVAL

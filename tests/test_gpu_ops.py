@@ -831,3 +831,106 @@ def test_slot_insertion_into_a_batched_cache_then_batched_decode(G):
     ref_out, _, _, _ = orc.decode_step(kc_before, vc_before, orc.bf16_bits_to_f64(qn), orc.bf16_bits_to_f64(kn),
                                        orc.bf16_bits_to_f64(vn), step, mult)
     U.assert_bf16_close(U.host(dout), ref_out, "batched decode after slot insertion")
+
+
+# --------------------------------------------------------------------------
+# Fused Q/K/V projection with RoPE and the cache write (prefill)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,d,Hq,Hkv,Tmax,steps", [
+    (2, 300, 256, 6, 2, 512, [0, 137]),     # ragged row tiles, two positions
+    (1, 77, 200, 4, 1, 77, None),           # step NULL: the cache is the prompt's K/V; K tail
+    (3, 64, 6144, 48, 8, 128, [64, 0, 10]),  # Grok-1 widths
+])
+def test_prefill_qkv_matches_projections_then_append(G, B, T, d, Hq, Hkv, Tmax, steps):
+    """Bit-identical to three grok_linear_int8 calls and grok_kv_append (which
+    rotates q and k with the same pinned arithmetic), and within tolerance of
+    the oracle's rope(x W) at the same positions; cache slots outside
+    [step, step + T) are untouched."""
+    grok, U, torch = G
+    g = gi.rng(d + T)
+    D = 128
+    xb = gi.normal_bf16(g, (B, T, d))
+    ws = {n: gi.int8_uniform(g, (d, h * D)) for n, h in (("q", Hq), ("k", Hkv), ("v", Hkv))}
+    sc = {n: (g.uniform(0.5, 1.5, w.shape[1]) / (127 * math.sqrt(d) * 0.58)).astype(np.float32)
+          for n, w in ws.items()}
+    kc0, vc0 = gi.normal_bf16(g, (B, Tmax, Hkv, D)), gi.normal_bf16(g, (B, Tmax, Hkv, D))
+    x = U.dev_bf16(xb)
+    W = {n: U.dev(w) for n, w in ws.items()}
+    S = {n: U.dev(s) for n, s in sc.items()}
+    st = None if steps is None else U.dev(np.array(steps, np.int32))
+    q = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    kc, vc = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    new_step = torch.zeros(B, dtype=torch.int32, device="cuda") if steps is not None else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(grok.grok_prefill_qkv_workspace_bytes(Tmax), dtype=torch.uint8, device="cuda")
+    grok.grok_prefill_qkv(x, W["q"], S["q"], W["k"], S["k"], W["v"], S["v"], q, kc, vc, wsp, step=st,
+                          new_step=new_step, status=status)
+    # unfused: three projections, then append (RoPE of q in place and of k into the cache)
+    q2 = torch.empty_like(q)
+    k2 = torch.empty((B, T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v2 = torch.empty_like(k2)
+    for out, n in ((q2, "q"), (k2, "k"), (v2, "v")):
+        grok.grok_linear_int8(x, W[n], S[n], out)
+    kc2, vc2 = U.dev_bf16(kc0), U.dev_bf16(vc0)
+    st2 = st if st is not None else torch.zeros(B, dtype=torch.int32, device="cuda")
+    grok.grok_kv_append(kc2, vc2, k2, v2, st2, q_inout=q2)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    np.testing.assert_array_equal(U.bits(q), U.bits(q2))
+    np.testing.assert_array_equal(U.bits(kc), U.bits(kc2))
+    np.testing.assert_array_equal(U.bits(vc), U.bits(vc2))
+    s0 = np.zeros(B, np.int64) if steps is None else np.array(steps)
+    if new_step is not None:
+        np.testing.assert_array_equal(new_step.cpu().numpy(), s0 + T)
+    kcb = U.bits(kc)
+    for b in range(B):
+        keep = np.ones(Tmax, bool)
+        keep[s0[b]:s0[b] + T] = False
+        np.testing.assert_array_equal(kcb[b, keep], kc0[b, keep])
+    # oracle on a few rows
+    x64 = orc.bf16_bits_to_f64(xb)
+    for b in range(B):
+        rows = np.array([0, T - 1, T // 2])
+        pos = (s0[b] + rows)[None]
+        qr = orc.rope(orc.linear_int8(x64[b, rows], ws["q"], sc["q"], out="bf16").reshape(1, len(rows), Hq, D), pos)
+        kr = orc.rope(orc.linear_int8(x64[b, rows], ws["k"], sc["k"], out="bf16").reshape(1, len(rows), Hkv, D), pos)
+        U.assert_bf16_close(U.host(q[b, rows])[None], qr, f"fused q b={b}")
+        U.assert_bf16_close(orc.bf16_bits_to_f64(kcb[b, s0[b] + rows])[None], kr, f"fused k b={b}")
+
+
+def test_prefill_qkv_out_of_range_sequence_writes_nothing(G):
+    grok, U, torch = G
+    g = gi.rng(5)
+    B, T, d, Hq, Hkv, Tmax, D = 2, 40, 64, 2, 1, 64, 128
+    x = U.dev_bf16(gi.normal_bf16(g, (B, T, d)))
+    w = {n: U.dev(gi.int8_uniform(g, (d, h * D))) for n, h in (("q", Hq), ("k", Hkv), ("v", Hkv))}
+    s = {n: torch.full((t.shape[1],), 1e-3, dtype=torch.float32, device="cuda") for n, t in w.items()}
+    q = torch.zeros((B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((B, Tmax, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    step = U.dev(np.array([30, 10], np.int32))   # sequence 0: 30 + 40 > 64
+    new_step = torch.zeros(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(grok.grok_prefill_qkv_workspace_bytes(Tmax), dtype=torch.uint8, device="cuda")
+    grok.grok_prefill_qkv(x, w["q"], s["q"], w["k"], s["k"], w["v"], s["v"], q, kc, vc, wsp, step=step,
+                          new_step=new_step, status=status)
+    torch.cuda.synchronize()
+    assert status.item() == -34
+    np.testing.assert_array_equal(new_step.cpu().numpy(), [30, 50])
+    assert not U.host(q[0]).any() and not U.host(kc[0]).any() and not U.host(vc[0]).any()
+    assert U.host(q[1]).any() and U.host(kc[1, 10:50]).any() and not U.host(kc[1, 50:]).any()
+
+
+def test_sublayer_fused_front_half_is_bit_identical(G):
+    """The sub-layer with the fused Q/K/V launch gives the bits of the one with
+    separate projections and RoPE passes."""
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    p = gi.make_sublayer_inputs(1, 300, 1024, 8, 2, 128, seed=12)
+    dv = {k: (U.dev_bf16(v) if k == "x" else U.dev(v)) for k, v in p.items()}
+    outs = []
+    for fused in (True, False):
+        st = pipe.SublayerStep(dv["x"], dv["wq"], dv["sq"], dv["wk"], dv["sk"], dv["wv"], dv["sv"], dv["wo"],
+                               dv["so"], 8, 2, 128, 1 / math.sqrt(128), fused=fused)
+        outs.append(U.bits(st()).copy())
+    np.testing.assert_array_equal(outs[0], outs[1])
