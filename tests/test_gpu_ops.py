@@ -329,6 +329,7 @@ def test_prefill_mfma(G, B, T, Hq, Hkv, scale):
     (2, 100, 6, 1, 256, [128, 5]),
     (1, 1, 16, 2, 64, [40]),             # one token: a decode step
     (2, 130, 12, 2, 400, [64, 270]),     # several query tiles
+    (3, 70, 12, 2, 12400, [4100, 12330, 9]),  # long cached prefixes next to a short one
 ])
 def test_prefill_chunk(G, B, T, Hq, Hkv, Tmax, offsets):
     grok, U, torch = G
