@@ -179,6 +179,20 @@ struct TileRing {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the unused prefetches
+    // Their registers pass through empty statements after the wait: the last
+    // D prefetches are never read, and without a use the compiler could hand
+    // their registers to other values while the loads are still in flight.
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+#pragma unroll
+      for (int v = 0; v < NB; ++v) asm volatile("" : "+v"(wr[u][v]));
+      if constexpr (!XL) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(xa[u][t][h]));
+      }
+    }
   }
 };
 
