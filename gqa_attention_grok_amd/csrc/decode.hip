@@ -12,8 +12,8 @@
 // head, split of 128 cache slots). The whole split -- 128 K rows and 128 V
 // rows of the head, 64 KB -- is requested up front: K straight into the
 // registers that feed the MFMA (each lane loads its own fragments), V HBM ->
-// LDS (global_load_lds) for the transpose reads. With 32 KB of LDS per
-// workgroup, three workgroups per CU keep up to 192 KB in flight and overlap
+// LDS (global_load_lds) for the transpose reads. With 33 KB of LDS per
+// workgroup, four workgroups per CU keep up to 256 KB in flight and overlap
 // one's loads with another's compute. Wave w owns slots 32w .. 32w+31 of the
 // split: it loads them itself (no barrier before the compute) and runs, with
 // the G <= 16 query heads of the KV head as MFMA rows (unused rows zero),
