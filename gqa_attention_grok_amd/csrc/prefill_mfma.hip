@@ -54,6 +54,7 @@ constexpr int kRowBlocks = kWaves * kRB;
 constexpr int kBN = 64;            // keys per tile (two halves of 32 per MFMA step)
 constexpr int kTileBytes = kBN * kRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSortMaxB = 64;      // chunked prefill: batches ordered by cached length up to this size
 
 struct PrefillArgs {
   const bf16_t *q, *k, *v;
@@ -89,8 +90,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   id /= a.Hkv;
   const int hc = id % a.nhc;
   id /= a.nhc;
-  const int qt = a.nqt - 1 - (id % a.nqt);
-  const int b = id / a.nqt;
+  int qt = a.nqt - 1 - (id % a.nqt);
+  int b = id / a.nqt;
+  if constexpr (kOffset) {
+    // Chunks after cached prefixes of different lengths: the work of a query
+    // tile grows with its sequence's offset. Items (sequence, query tile) are
+    // ranked by work -- sequences by offset, longest first, then query tiles
+    // longest first -- and the first half of the grid takes them from the
+    // longest end, the second half from the shortest, so that the workgroups
+    // resident together on a CU pair long items with short ones.
+    __shared__ int seq_by_len[kSortMaxB];
+    if (a.B <= kSortMaxB) {  // uniform
+      if (tid < a.B) {
+        const int ot = a.offset[tid];
+        int rank = 0;
+        for (int j = 0; j < a.B; ++j) {
+          const int oj = a.offset[j];
+          rank += (oj > ot || (oj == ot && j < tid)) ? 1 : 0;
+        }
+        seq_by_len[rank] = tid;
+      }
+      __syncthreads();
+      const int V = a.B * a.nqt, h = (V + 1) / 2;
+      const int u = id < h ? id : V - 1 - (id - h);
+      b = seq_by_len[u / a.nqt];
+      qt = a.nqt - 1 - (u % a.nqt);
+    }
+  }
   const int span = 16 * a.npb;
   // o: position of row 0; klen: keys [0, klen) exist (prefix + this chunk)
   const int o = kOffset ? a.offset[b] : 0;

@@ -330,6 +330,8 @@ def test_prefill_mfma(G, B, T, Hq, Hkv, scale):
     (1, 1, 16, 2, 64, [40]),             # one token: a decode step
     (2, 130, 12, 2, 400, [64, 270]),     # several query tiles
     (3, 70, 12, 2, 12400, [4100, 12330, 9]),  # long cached prefixes next to a short one
+    (7, 20, 12, 2, 200, [150, 0, 75, 180, 3, 150, 90]),  # work ranking with a tie
+    (65, 5, 6, 1, 48, [(7 * i) % 44 for i in range(65)]),  # more sequences than the ranking takes
 ])
 def test_prefill_chunk(G, B, T, Hq, Hkv, Tmax, offsets):
     grok, U, torch = G
