@@ -1,0 +1,150 @@
+"""GPU parity against the fp64 oracle on seeded random shapes: prefill (bf16
+MFMA path, optional key padding; fp32 generic path), decode (plain and with the
+append fused) and chunked prefill after cached prefixes. The shapes are drawn
+once from a fixed seed, so every run checks the same cases; each case prints
+its shape in the test id."""
+import math
+
+import numpy as np
+import pytest
+
+import gqa_inputs as gi
+import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+_rng = np.random.default_rng(20261202)
+
+
+def _heads():
+    hkv = int(_rng.choice([1, 2, 4, 8]))
+    return hkv * int(_rng.choice([1, 2, 3, 6])), hkv
+
+
+def _prefill_cases(n):
+    out = []
+    for _ in range(n):
+        hq, hkv = _heads()
+        out.append((int(_rng.integers(1, 4)), int(_rng.integers(1, 201)), hq, hkv,
+                    float(_rng.choice([1.0, 4.0])), bool(_rng.integers(0, 2)), int(_rng.integers(0, 1 << 30))))
+    return out
+
+
+def _decode_cases(n):
+    out = []
+    for _ in range(n):
+        hq, hkv = _heads()
+        B, Tmax = int(_rng.integers(1, 6)), int(_rng.integers(64, 701))
+        lens = [int(x) for x in _rng.integers(1, Tmax + 1, size=B)]
+        out.append((hq, hkv, Tmax, lens, int(_rng.integers(0, 1 << 30))))
+    return out
+
+
+def _chunk_cases(n):
+    out = []
+    for _ in range(n):
+        hq, hkv = _heads()
+        B, T = int(_rng.integers(1, 5)), int(_rng.integers(1, 101))
+        Tmax = T + int(_rng.integers(0, 501))
+        offsets = [int(x) for x in _rng.integers(0, Tmax - T + 1, size=B)]
+        out.append((hq, hkv, T, Tmax, offsets, int(_rng.integers(0, 1 << 30))))
+    return out
+
+
+PREFILL = _prefill_cases(8)
+DECODE = _decode_cases(6)
+CHUNK = _chunk_cases(6)
+
+
+@pytest.fixture(scope="module")
+def G():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gqa_attention_grok_amd as grok
+    import gpu_util
+    return grok, gpu_util, torch
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,scale,padded,seed", PREFILL,
+                         ids=[f"B{c[0]}-T{c[1]}-Hq{c[2]}-Hkv{c[3]}-x{c[4]:g}-pad{int(c[5])}" for c in PREFILL])
+def test_random_prefill_bf16(G, B, T, Hq, Hkv, scale, padded, seed):
+    grok, U, torch = G
+    D = 128
+    mult = scale / math.sqrt(D)
+    p = gi.make_prefill_inputs(B, T, Hq, Hkv, D, seed=seed, dtype="bf16", key_pad_frac=0.1 if padded else 0.0)
+    pad = p.get("key_valid") if padded else None
+    out = torch.empty((B, T, Hq * D), dtype=torch.bfloat16, device="cuda")
+    grok.grok_attn_prefill(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), out, mult, 30.0,
+                           key_valid=None if pad is None else U.dev(pad))
+    to64 = orc.bf16_bits_to_f64
+    mask = orc.attention_mask(np.broadcast_to(np.arange(T), (B, T)), T, key_valid=pad)
+    ref = orc.attention(to64(p["q"]), to64(p["k"]), to64(p["v"]), mask, mult, 30.0)
+    U.assert_bf16_close(U.host(out), ref, f"random prefill B={B} T={T} Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_random_prefill_f32_generic(G, case):
+    grok, U, torch = G
+    rng = np.random.default_rng(4000 + case)
+    D = int(rng.choice([8, 32, 64]))
+    hkv = int(rng.choice([1, 2]))
+    Hq, B, T = hkv * int(rng.choice([1, 3])), int(rng.integers(1, 3)), int(rng.integers(1, 40))
+    p = gi.make_prefill_inputs(B, T, Hq, hkv, D, seed=5000 + case, dtype="f32")
+    out = torch.empty((B, T, Hq * D), dtype=torch.float32, device="cuda")
+    mult = 1 / math.sqrt(D)
+    grok.grok_attn_prefill(U.dev(p["q"]), U.dev(p["k"]), U.dev(p["v"]), out, mult, 30.0)
+    mask = orc.attention_mask(np.broadcast_to(np.arange(T), (B, T)), T)
+    ref = orc.attention(p["q"].astype(np.float64), p["k"].astype(np.float64), p["v"].astype(np.float64), mask,
+                        mult, 30.0)
+    U.assert_f32_close(U.host(out), ref, f"random f32 prefill B={B} T={T} Hq={Hq} Hkv={hkv} D={D}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,Tmax,lens,seed", DECODE,
+                         ids=[f"Hq{c[0]}-Hkv{c[1]}-Tmax{c[2]}-B{len(c[3])}" for c in DECODE])
+def test_random_decode(G, Hq, Hkv, Tmax, lens, seed):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    B, D = len(lens), 128
+    mult = 1 / math.sqrt(D)
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=seed, lengths=lens)
+    kv_len = np.asarray(lens, np.int32)
+    to64 = orc.bf16_bits_to_f64
+    # plain decode over caches that already hold every attended slot
+    out = torch.empty((B, 1, Hq * D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+    grok.grok_attn_decode(U.dev_bf16(p["q"]), U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"]), U.dev(kv_len),
+                          out, ws, mult)
+    mask = orc.attention_mask((kv_len - 1)[:, None], Tmax, kv_len=kv_len)
+    ref = orc.attention(to64(p["q"]), to64(p["k_cache"]), to64(p["v_cache"]), mask, mult, 30.0)
+    U.assert_bf16_close(U.host(out), ref, f"random decode lens={lens}")
+    # the fused step (RoPE + append of the new token, then attention) is a
+    # one-token chunk at offset step[b] for the oracle
+    kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    st = pipe.DecodeStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                         U.dev(p["step"]), mult)
+    got = U.host(st())
+    torch.cuda.synchronize()
+    assert st.status.item() == 0
+    ref2, _, _, _ = orc.chunk_prefill(to64(p["k_cache"]), to64(p["v_cache"]), to64(p["q"]), to64(p["k_new"]),
+                                      to64(p["v_new"]), p["step"], mult)
+    U.assert_bf16_close(got, ref2, f"random fused decode lens={lens}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,T,Tmax,offsets,seed", CHUNK,
+                         ids=[f"Hq{c[0]}-Hkv{c[1]}-T{c[2]}-Tmax{c[3]}-B{len(c[4])}" for c in CHUNK])
+def test_random_prefill_chunk(G, Hq, Hkv, T, Tmax, offsets, seed):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    B, D = len(offsets), 128
+    mult = 1 / math.sqrt(D)
+    p = gi.make_chunk_inputs(B, T, Hq, Hkv, D, Tmax, seed=seed, offsets=offsets)
+    kc, vc = U.dev_bf16(p["k_cache"]), U.dev_bf16(p["v_cache"])
+    st = pipe.ChunkStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                        U.dev(p["step"]), mult)
+    out = U.host(st())
+    torch.cuda.synchronize()
+    assert st.status.item() == 0
+    to64 = orc.bf16_bits_to_f64
+    ref, _, _, _ = orc.chunk_prefill(to64(p["k_cache"]), to64(p["v_cache"]), to64(p["q"]), to64(p["k_new"]),
+                                     to64(p["v_new"]), p["step"], mult)
+    U.assert_bf16_close(out, ref, f"random chunk T={T} offsets={offsets}")
