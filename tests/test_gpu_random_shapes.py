@@ -1,6 +1,7 @@
 """GPU parity against the fp64 oracle on seeded random shapes: prefill (bf16
 MFMA path, optional key padding; fp32 generic path), decode (plain and with the
-append fused) and chunked prefill after cached prefixes. The shapes are drawn
+append fused), chunked prefill after cached prefixes, RMSNorm and the int8
+Linears (tiled and few-row). The shapes are drawn
 once from a fixed seed, so every run checks the same cases; each case prints
 its shape in the test id."""
 import math
@@ -148,3 +149,61 @@ def test_random_prefill_chunk(G, Hq, Hkv, T, Tmax, offsets, seed):
     ref, _, _, _ = orc.chunk_prefill(to64(p["k_cache"]), to64(p["v_cache"]), to64(p["q"]), to64(p["k_new"]),
                                      to64(p["v_new"]), p["step"], mult)
     U.assert_bf16_close(out, ref, f"random chunk T={T} offsets={offsets}")
+
+
+_rng2 = np.random.default_rng(20261203)
+NORM = [(int(_rng2.integers(1, 51)), int(_rng2.integers(1, 9001)), bool(_rng2.integers(0, 2)),
+         bool(_rng2.integers(0, 2)), str(_rng2.choice(["bf16", "f32"]))) for _ in range(5)]
+LINEAR = [(int(_rng2.integers(1, 601)), 8 * int(_rng2.integers(1, 401)), 8 * int(_rng2.integers(1, 301)))
+          for _ in range(4)]
+GEMV = [(int(_rng2.integers(1, 81)), 8 * int(_rng2.integers(1, 801)),
+         tuple(8 * int(n) for n in _rng2.integers(1, 201, size=int(_rng2.integers(1, 4))))) for _ in range(4)]
+
+
+@pytest.mark.parametrize("rows,d,use_gamma,use_res,dtype", NORM,
+                         ids=[f"r{c[0]}-d{c[1]}-g{int(c[2])}-res{int(c[3])}-{c[4]}" for c in NORM])
+def test_random_rmsnorm(G, rows, d, use_gamma, use_res, dtype):
+    grok, U, torch = G
+    g = gi.rng(rows * 7 + d)
+    if dtype == "bf16":
+        xb, rb = gi.normal_bf16(g, (rows, d)), gi.normal_bf16(g, (rows, d))
+        x, r = U.dev_bf16(xb), U.dev_bf16(rb)
+        x64, r64 = orc.bf16_bits_to_f64(xb), orc.bf16_bits_to_f64(rb)
+    else:
+        xf, rf = gi.normal_f32(g, (rows, d)) * 3, gi.normal_f32(g, (rows, d))
+        x, r = U.dev(xf), U.dev(rf)
+        x64, r64 = xf.astype(np.float64), rf.astype(np.float64)
+    gam = g.uniform(0.5, 1.5, d).astype(np.float32) if use_gamma else None
+    y = torch.empty_like(x)
+    grok.grok_rmsnorm(x, y, gamma=U.dev(gam) if use_gamma else None, residual=r if use_res else None)
+    ref = r64 + orc.rmsnorm(x64, gam, 1e-5, out=dtype) if use_res else orc.rmsnorm(x64, gam, 1e-5)
+    if dtype == "bf16":
+        U.assert_bf16_close(U.host(y), ref, f"random rmsnorm rows={rows} d={d}")
+    else:
+        U.assert_f32_close(U.host(y), ref, f"random rmsnorm rows={rows} d={d}")
+
+
+@pytest.mark.parametrize("M,K,N", LINEAR, ids=[f"M{c[0]}-K{c[1]}-N{c[2]}" for c in LINEAR])
+def test_random_linear_int8(G, M, K, N):
+    grok, U, torch = G
+    g = gi.rng(M * 3 + K + N)
+    xb, w = gi.normal_bf16(g, (M, K)), gi.int8_uniform(g, (K, N))
+    s = (0.02 / 127 * g.uniform(0.5, 1.5, N)).astype(np.float32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    grok.grok_linear_int8(U.dev_bf16(xb), U.dev(w), U.dev(s), y)
+    U.assert_bf16_close(U.host(y), orc.linear_int8(orc.bf16_bits_to_f64(xb), w, s), f"random linear M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,Ns", GEMV, ids=[f"M{c[0]}-K{c[1]}-N{'_'.join(map(str, c[2]))}" for c in GEMV])
+def test_random_gemv(G, M, K, Ns):
+    grok, U, torch = G
+    g = gi.rng(M * 5 + K + sum(Ns))
+    xb = gi.normal_bf16(g, (M, K))
+    ws = [gi.int8_uniform(g, (K, n)) for n in Ns]
+    ss = [(0.02 / 127 * g.uniform(0.5, 1.5, n)).astype(np.float32) for n in Ns]
+    wp = [grok.grok_linear_int8_pack(U.dev(w)) for w in ws]
+    ys = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in Ns]
+    grok.grok_linear_int8_gemv(U.dev_bf16(xb), wp, [U.dev(s) for s in ss], ys)
+    x64 = orc.bf16_bits_to_f64(xb)
+    for p in range(len(Ns)):
+        U.assert_bf16_close(U.host(ys[p]), orc.linear_int8(x64, ws[p], ss[p]), f"random gemv M={M} K={K} matrix {p}")
