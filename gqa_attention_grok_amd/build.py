@@ -1,8 +1,9 @@
 """Compile the HIP library ``libgrokattn.so`` for gfx950, in-tree.
 
-``python gqa_attention_grok_amd/build.py`` (or ``build()``) runs hipcc once
-over every ``csrc/*.hip`` file and links them into one shared library next to
-this file. hipcc cross-compiles for gfx950 without a GPU present.
+``python gqa_attention_grok_amd/build.py`` (or ``build()``) compiles every
+``csrc/*.hip`` file to an object (in parallel, with the per-file flags below)
+and links them into one shared library next to this file. hipcc
+cross-compiles for gfx950 without a GPU present.
 """
 from __future__ import annotations
 
@@ -11,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,7 +23,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     f"--offload-arch={ARCH}",
     # Keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -30,6 +31,15 @@ HIPCC_FLAGS = [
     "-Wno-unknown-pragmas",
     "-fvisibility=hidden",
 ]
+
+
+# Extra flags for single files. The tiled int8 product runs its grouped (MoE)
+# instantiations about 3.5 % faster under the backend's ILP-maximising machine
+# scheduler, with the other instantiations unchanged; the attention kernels are
+# slower under it, so it applies to this file only.
+PER_FILE_FLAGS = {
+    "linear_int8.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def sources():
@@ -43,20 +53,32 @@ def hipcc():
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    """Build libgrokattn.so; returns its path. Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature: harmless.
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libgrokattn.so; returns its path. Always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmp = LIB + ".tmp"
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    with tempfile.TemporaryDirectory(prefix="grokattn_build_") as objdir:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
+            extra = PER_FILE_FLAGS.get(os.path.basename(src), [])
+            jobs.append(([hipcc(), *HIPCC_FLAGS, *extra, *inc, "-c", src, "-o", obj], obj))
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda j: _run(j[0], verbose), jobs))
+        _run([hipcc(), "-shared", f"--offload-arch={ARCH}", *[o for _, o in jobs], "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
