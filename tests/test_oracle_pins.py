@@ -570,3 +570,17 @@ def test_moe_routes_each_token_to_its_own_experts():
         mix = sum(gates[0, t, k] * orc.expert_ffn(n[t:t + 1], *exps[idx[0, t, k]], io=None)[0] for k in range(2))
         np.testing.assert_allclose(y[0, t], x[0, t] + orc.rmsnorm(mix, None, 1e-5), rtol=1e-10, atol=1e-10)
     assert len(np.unique(idx)) > 2  # the tokens do not all pick the same pair
+
+
+def test_expert_ffn_gelu_on_the_gate_branch_before_the_product():
+    """Hand examples at d = F = 1 (tests/golden/expert_ffn_d1.txt): the GELU
+    acts on the gate projection alone, before the product with the value
+    projection ([ch6] §6.2). Expected values are x*Phi(x) from the standard
+    normal CDF; the tanh form used by the oracle is within 2e-3 relative of
+    them, while GELU on the value branch or after the product is off by 15 %
+    or more on the first row."""
+    for x, wg, wv, w1, want in (map(float, r) for r in read_golden_rows("expert_ffn_d1.txt")):
+        one = lambda f: (np.full((1, 1), 127, np.int8), np.array([f / 127], np.float32))
+        (ag, sg), (av, sv), (a1, s1) = one(wg), one(wv), one(w1)
+        got = orc.expert_ffn(np.array([[x]]), ag, sg, av, sv, a1, s1, io=None)[0, 0]
+        assert abs(got - want) <= 2e-3 * abs(want), (x, wg, wv, w1, got, want)
