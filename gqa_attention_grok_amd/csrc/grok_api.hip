@@ -29,6 +29,13 @@ int hip_status(hipError_t e, const char *what) {
   return fail(GROK_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// True when the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 bool bad_softmax_params(float mult, float cap) {
   return !isfinite(mult) || !(cap > 0.f) || cap > 40.f;
 }
@@ -72,6 +79,8 @@ int grok_linear_int8(const void *x, const int8_t *w, const float *scales, void *
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(scales)) % 16 ||
       (reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(y)) % 8)
     return fail(GROK_EINVAL, "linear_int8: misaligned pointer");
+  if (overlaps(x, static_cast<size_t>(M) * K * 2, y, static_cast<size_t>(M) * N * 2))
+    return fail(GROK_EINVAL, "linear_int8: y overlaps x");
   return hip_status(grok::launch_linear_int8(x, w, scales, y, M, K, N, stream), "linear_int8");
 }
 
@@ -115,6 +124,9 @@ int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w_pack
     a2 |= reinterpret_cast<uintptr_t>(y[p]);
   }
   if (a16 % 16 || a4 % 4 || a2 % 2) return fail(GROK_EINVAL, "linear_int8_gemv: misaligned pointer");
+  for (int p = 0; p < n_mats; ++p)
+    if (overlaps(x, static_cast<size_t>(M) * K * 2, y[p], static_cast<size_t>(M) * N[p] * 2))
+      return fail(GROK_EINVAL, "linear_int8_gemv: y[%d] overlaps x", p);
   return hip_status(grok::launch_linear_int8_gemv(x, n_mats, w_packed, scales, y, N, M, K, stream),
                     "linear_int8_gemv");
 }
@@ -145,6 +157,8 @@ int grok_decode_qkv(const void *x, const float *gamma, float eps, int prenorm,
   const uintptr_t a2 = reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(k_cache) |
                        reinterpret_cast<uintptr_t>(v_cache);
   if (a16 % 16 || a4 % 4 || a2 % 2) return fail(GROK_EINVAL, "decode_qkv: misaligned pointer");
+  if (overlaps(x, static_cast<size_t>(B) * d * 2, q_out, static_cast<size_t>(B) * Hq * D * 2))
+    return fail(GROK_EINVAL, "decode_qkv: q_out overlaps x");
   grok::RopeFreqs f;
   grok::rope_build_freqs(D, rope_base, &f);
   const int8_t *w[3] = {wq_packed, wk_packed, wv_packed};
@@ -176,6 +190,7 @@ int grok_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *
   if (q_inout && (Hq < 1 || Hq % Hkv)) return fail(GROK_EINVAL, "kv_append: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
   if (!k_cache || !v_cache || !k_new || !v_new || !step) return fail(GROK_EINVAL, "kv_append: null pointer");
   if (!isfinite(rope_base)) return fail(GROK_EINVAL, "kv_append: bad rope_base");
+  if (new_step && new_step == step) return fail(GROK_EINVAL, "kv_append: new_step must not alias step");
   const uintptr_t al = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
                        reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
                        reinterpret_cast<uintptr_t>(q_inout);
@@ -262,6 +277,8 @@ int grok_attn_decode_append(const void *q, const void *k_new, const void *v_new,
                        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
                        reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(workspace);
   if (al % 16) return fail(GROK_EINVAL, "attn_decode_append: misaligned pointer");
+  if (overlaps(q, static_cast<size_t>(B) * Hq * D * 2, q_out, static_cast<size_t>(B) * Hq * D * 2))
+    return fail(GROK_EINVAL, "attn_decode_append: q_out overlaps q");
   const size_t need = grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);
   if (ws_bytes < need)
     return fail(GROK_ENOMEM, "attn_decode_append: workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -399,6 +416,8 @@ int grok_prefill_qkv(const void *x, const int8_t *wq, const float *sq, const int
   const uintptr_t a8 = reinterpret_cast<uintptr_t>(wq) | reinterpret_cast<uintptr_t>(wk) |
                        reinterpret_cast<uintptr_t>(wv);
   if (a16 % 16 || a8 % 8) return fail(GROK_EINVAL, "prefill_qkv: misaligned pointer");
+  if (overlaps(x, static_cast<size_t>(B) * T * d * 2, q_out, static_cast<size_t>(B) * T * Hq * D * 2))
+    return fail(GROK_EINVAL, "prefill_qkv: q_out overlaps x");
   const size_t need = grok::prefill_qkv_workspace_bytes(Tmax);
   if (ws_bytes < need) return fail(GROK_ENOMEM, "prefill_qkv: workspace %zu bytes < %zu needed", ws_bytes, need);
   grok::PrefillQkvArgs qa = {};

@@ -77,12 +77,12 @@ GROK_API int grok_rmsnorm(const void *x, const float *gamma, const void *residua
  *   x       [M, K] bf16 activations.
  *   w       [K, N] int8 weights (input axis first, as the pages store them).
  *   scales  [N] fp32, one per output channel (broadcast along K).
- *   y       [M, N] bf16.
+ *   y       [M, N] bf16, must not overlap x.
  * The int8 values are used exactly (|w| <= 127 is exact in bf16), products are
  * accumulated in fp32, and the channel scale is applied to the fp32 sum before
  * rounding to bf16.
- * Errors: EINVAL for NULL pointers, M < 0, K < 1, N < 1, or K or N not a
- * multiple of 8. M == 0 is a no-op.
+ * Errors: EINVAL for NULL pointers, M < 0, K < 1, N < 1, K or N not a
+ * multiple of 8, misaligned pointers, or y overlapping x. M == 0 is a no-op.
  */
 GROK_API int grok_linear_int8(const void *x, const int8_t *w, const float *scales, void *y,
                      int64_t M, int K, int N, hipStream_t stream);
@@ -120,7 +120,8 @@ GROK_API int grok_linear_int8_pack(const int8_t *w, int8_t *w_packed, int K, int
  *              matrix (16-byte aligned), scales[p] [N[p]] fp32, y[p]
  *              [M, N[p]] bf16 (must not overlap x or each other).
  * Errors: EINVAL for NULL pointers, n_mats outside [1, 3], M < 0, K or N[p]
- * not a positive multiple of 8, or misaligned pointers. M == 0 is a no-op.
+ * not a positive multiple of 8, misaligned pointers, or a y[p] overlapping x.
+ * M == 0 is a no-op.
  */
 GROK_API int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *const *w_packed,
                                    const float *const *scales, void *const *y, const int *N,
@@ -148,7 +149,8 @@ GROK_API int grok_linear_int8_gemv(const void *x, int n_mats, const int8_t *cons
  *            GROK_ERANGE is stored to *status.
  * Errors: EINVAL for NULL pointers, sizes < 1, d not a multiple of 8, D !=
  * 128, Hq % Hkv != 0, bad rope_base or eps, misaligned pointers, new_step ==
- * step, or prenorm with B above what fits on chip (4 rows of width <= 8192).
+ * step, q_out overlapping x, or prenorm with B above what fits on chip (4
+ * rows of width <= 8192).
  */
 GROK_API int grok_decode_qkv(const void *x, const float *gamma, float eps, int prenorm,
                              const int8_t *wq_packed, const float *sq, const int8_t *wk_packed,
@@ -182,12 +184,14 @@ GROK_API int grok_rope(void *x, int B, int T, int H, int D, const int32_t *offse
  * With rope_base <= 0 no rotation is applied (k is copied bit for bit).
  * No other cache slot is touched. All tensors bf16:
  *   caches [B, Tmax, Hkv, D]; k_new, v_new [B, T, Hkv, D]; q_inout [B, T, Hq, D].
- *   step   [B] int32 device array; new_step may alias step.
+ *   step   [B] int32 device array; new_step must not alias step (the
+ *          workgroups of a sequence read step[b] while its new_step[b] is
+ *          written).
  * A sequence with step[b] < 0 or step[b] + T > Tmax is skipped entirely (no
  * write, new_step[b] = step[b]) and GROK_ERANGE is stored to *status.
  * Errors: EINVAL for NULL required pointers, sizes < 1 (B, T, Tmax, Hkv, D),
  * Hq not a multiple of Hkv (when q_inout is given), D not a multiple of 16 or
- * D > 512, T > Tmax, or a pointer not 16-byte aligned.
+ * D > 512, T > Tmax, a pointer not 16-byte aligned, or new_step == step.
  */
 GROK_API int grok_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
                    void *q_inout, const int32_t *step, int32_t *new_step, int32_t *status,
@@ -284,7 +288,9 @@ GROK_API int grok_attn_decode(const void *q, const void *k_cache, const void *v_
  * output row, new_step[b] = step[b], and GROK_ERANGE is stored to *status.
  * Errors: EINVAL for NULL pointers, sizes < 1, Hq % Hkv != 0, Hq/Hkv > 16,
  * D != 128, bad attn_mult/softcap (as for prefill) or rope_base, a misaligned
- * pointer (16 bytes), or new_step == step; ENOMEM if ws_bytes is too small.
+ * pointer (16 bytes), new_step == step, or q_out overlapping q (every split of
+ * a sequence reads q while the first one writes q_out); ENOMEM if ws_bytes
+ * is too small.
  */
 GROK_API int grok_attn_decode_append(const void *q, const void *k_new, const void *v_new,
                                      void *k_cache, void *v_cache, const int32_t *step,
@@ -311,13 +317,15 @@ GROK_API size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hk
  *   x [B, T, d] bf16 (the normalised rows); wq [d, Hq*128], wk, wv
  *   [d, Hkv*128] int8; sq, sk, sv fp32 channel scales; q_out [B, T, Hq, 128];
  *   caches [B, Tmax, Hkv, 128] bf16; step [B] int32 device or NULL;
+ *   q_out must not overlap x;
  *   workspace: device, grok_prefill_qkv_workspace_bytes(Tmax, 128) bytes (a
  *   cos/sin table of every cache position, rebuilt by each call).
  * A sequence with s < 0 or s + T > Tmax gets no writes at all (q_out rows
  * untouched), new_step[b] = s, and GROK_ERANGE is stored to *status.
  * Errors: EINVAL for NULL pointers, sizes < 1, D != 128, T > Tmax, d not a
- * multiple of 8, a bad rope_base, new_step == step, or a misaligned pointer
- * (16 bytes; the weights 8); ENOMEM if ws_bytes is too small.
+ * multiple of 8, a bad rope_base, new_step == step, q_out overlapping x, or a
+ * misaligned pointer (16 bytes; the weights 8); ENOMEM if ws_bytes is too
+ * small.
  */
 GROK_API size_t grok_prefill_qkv_workspace_bytes(int Tmax, int D);
 GROK_API int grok_prefill_qkv(const void *x, const int8_t *wq, const float *sq, const int8_t *wk,

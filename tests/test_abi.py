@@ -92,6 +92,10 @@ def test_linear_validation(lib):
     assert _c(lib, "grok_linear_int8", FAKE, None, FAKE, FAKE, i64(4), i(16), i(16), None) == EINVAL
     assert _c(lib, "grok_linear_int8", ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, i64(4), i(16), i(16), None) == EINVAL
     assert _c(lib, "grok_linear_int8", None, None, None, None, i64(0), i(16), i(16), None) == 0
+    # y overlapping x (in place): every column tile reads all of x's rows
+    assert _c(lib, "grok_linear_int8", FAKE, FAKE, FAKE, ctypes.c_void_p(0x10000 + 4 * 16 * 2 - 8), i64(4), i(16),
+              i(16), None) == EINVAL
+    assert "overlaps x" in _err(lib)
 
 
 def test_rope_validation(lib):
@@ -116,6 +120,9 @@ def test_kv_append_validation(lib):
     bad = list(args)
     bad[0] = ctypes.c_void_p(0x10002)    # misaligned cache
     assert call(a=bad) == EINVAL
+    bad = list(args)
+    bad[6] = FAKE                        # new_step aliases step: a sequence's blocks read step[b] while it is written
+    assert call(a=bad) == EINVAL and "alias" in _err(lib)
 
 
 def test_prefill_validation(lib):
@@ -197,6 +204,7 @@ def test_pack_and_gemv_validation(lib):
     assert call(n_mats=2, N=Ns(6144, 1024), w=arr(0x10000, None, 0x10000)) == EINVAL
     assert call(M=-1) == EINVAL
     assert call(M=0, x=None) == 0
+    assert call() == EINVAL and "overlaps x" in _err(lib)     # y[0] in place over x
 
 
 def test_decode_qkv_validation(lib):
@@ -221,6 +229,7 @@ def test_decode_qkv_validation(lib):
     assert call(prenorm=1, B=4, d=16384) == EINVAL         # 4 x 16384 values do not fit either
     assert "at most 2 rows" in _err(lib)
     assert call(prenorm=1, B=1, eps=-1.0) == EINVAL
+    assert call(q=FAKE) == EINVAL and "overlaps x" in _err(lib)
 
 
 def test_decode_append_validation(lib):
@@ -243,6 +252,8 @@ def test_decode_append_validation(lib):
     assert call(q=None) == EINVAL
     assert call(new_step=FAKE) == EINVAL   # aliases step
     assert call(q_out=ctypes.c_void_p(0x10008)) == EINVAL
+    assert call(q_out=FAKE) == EINVAL and "overlaps q" in _err(lib)       # split 0 writes q_out while others read q
+    assert call(q_out=ctypes.c_void_p(0x10000 + 48 * 256 - 16)) == EINVAL  # partial overlap
 
 
 def test_prefill_chunk_validation(lib):
@@ -320,5 +331,6 @@ def test_prefill_qkv_validation(lib):
     assert call(new_step=FAKE) == EINVAL                   # aliases step
     assert call(q=ctypes.c_void_p(0x10008)) == EINVAL      # 16-byte alignment
     assert call(wq=ctypes.c_void_p(0x10004)) == EINVAL     # weights: 8 bytes
-    assert call(ws_bytes=16) == ENOMEM
+    assert call(ws_bytes=16, q=ctypes.c_void_p(0x400000)) == ENOMEM
     assert call(B=0) == EINVAL
+    assert call(q=FAKE) == EINVAL and "overlaps x" in _err(lib)
