@@ -265,32 +265,124 @@ def bench_moe(torch, grok, pipe, U, gi, steps, warmup):
             "kernel_ms": kern_ms, "kernel_tflops": flop / (kern_ms * 1e-3) / 1e12}
 
 
-def cpu_baseline(gi, orc):
-    """The fp64 oracle on a bounded sample of the 8k prefill: all 48 heads of
-    256 query rows spread over the sequence (RoPE of the sampled q rows and of
-    all keys, then the causal softcapped attention of those rows)."""
+# ---------------------------------------------------------------------------
+# The fp64 oracle timed on the host's cores (a reported baseline, not a target).
+# Runs in worker processes started with "spawn" before this process touches
+# the GPU; the workers import only the oracle and the input generator.
+# ---------------------------------------------------------------------------
+_W = {}
+
+
+def _oracle_init(name, k_bits=None, v_bits=None):
+    """Worker set-up (untimed): for the 8k prefill, the keys rotated at
+    positions 0..T-1 and the values in float64."""
+    import gqa_inputs as gi
+    import oracle as orc
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)  # one core per worker process
+    w = gi.WORKLOADS[name]
+    _W.update(w=w, orc=orc)
+    if k_bits is not None:
+        _W["k"] = orc.rope(orc.bf16_bits_to_f64(k_bits), np.arange(w.T)[None], out="bf16")
+        _W["v"] = orc.bf16_bits_to_f64(v_bits)
+
+
+def _oracle_prefill_rows(task):
+    """Causal softcapped attention of the given query rows (all heads)."""
+    rows, q_bits = task
+    w, orc = _W["w"], _W["orc"]
+    q = orc.rope(orc.bf16_bits_to_f64(q_bits), rows[None], out="bf16")
+    mask = orc.attention_mask(rows[None], w.T)
+    for c in range(0, len(rows), 8):  # bounded memory: 8 rows at a time
+        orc.attention(q[:, c:c + 8], _W["k"], _W["v"], mask[:, c:c + 8], w.attn_mult, w.softcap, out="bf16")
+    return len(rows)
+
+
+def _oracle_decode_seq(task):
+    """One sequence of a decode workload: RoPE of q and the new k, the append,
+    attention over the valid slots of its whole cache."""
+    kc, vc, q, kn, vn, step = task
+    w, orc = _W["w"], _W["orc"]
+    f = orc.bf16_bits_to_f64
+    orc.decode_step(f(kc), f(vc), f(q), f(kn), f(vn), step, w.attn_mult, w.softcap)
+    return 0
+
+
+def _noop(i):
+    time.sleep(0.2)  # keeps each worker busy long enough that all of them start
+    return i
+
+
+def _timed_pool(name, fn, tasks, workers, initargs=()):
+    """Wall time of fn over tasks on `workers` spawned processes (set-up excluded)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                             initializer=_oracle_init, initargs=(name, *initargs)) as ex:
+        list(ex.map(_noop, range(workers)))  # every worker has run its set-up
+        t0 = time.perf_counter()
+        list(ex.map(fn, tasks))
+        return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline():
+    """The fp64 oracle (NumPy, one thread per worker process) on the host cores:
+    a bounded sample of the 8k prefill (all 48 heads of 12 query rows per
+    worker, spread over the sequence), and the tiny fp32 prefill, the
+    one-sequence decode and the 32-sequence ragged decode in full."""
+    import gqa_inputs as gi
+    import oracle as orc
+    workers = max(1, min(16, os.cpu_count() or 1))
     w = gi.WORKLOADS["prefill_b1_t8192"]
     p = gi.make_workload(w.name)
     T = w.T
-    rows = np.linspace(0, T - 1, 256).astype(np.int64)
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):  # the oracle runs on one host core
-        return _cpu_baseline_sample(gi, orc, w, p, T, rows)
-
-
-def _cpu_baseline_sample(gi, orc, w, p, T, rows):
-    t0 = time.perf_counter()
-    k = orc.rope(orc.bf16_bits_to_f64(p["k"]), np.arange(T)[None], out="bf16")
-    v = orc.bf16_bits_to_f64(p["v"])
-    q = orc.rope(orc.bf16_bits_to_f64(p["q"][:, rows]), rows[None], out="bf16")
-    mask = orc.attention_mask(rows[None], T)
-    for c in range(0, len(rows), 8):  # bounded memory: 8 rows at a time
-        orc.attention(q[:, c:c + 8], k, v, mask[:, c:c + 8], w.attn_mult, w.softcap, out="bf16")
-    sec = time.perf_counter() - t0
+    rows = np.linspace(0, T - 1, 12 * workers).astype(np.int64)
+    # one task per worker, rows interleaved so that each holds short and long rows
+    tasks = [(rows[i::workers], p["q"][:, rows[i::workers]]) for i in range(workers)]
+    sec = _timed_pool(w.name, _oracle_prefill_rows, tasks, workers, (p["k"], p["v"]))
+    del p, tasks
     flop = int(sum(4 * w.D * w.Hq * (int(t) + 1) for t in rows))
-    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(rows)} of {T} query rows (all 48 heads) of the 8k prefill, "
-                      f"incl. RoPE of all keys; {flop} flop in {sec:.1f} s, single-threaded NumPy"}
+    extra = {}
+    wt = gi.WORKLOADS["prefill_f32_t16"]
+    pt = gi.make_workload(wt.name)
+    pos = np.arange(wt.T)[None]
+    t0 = time.perf_counter()
+    for _ in range(5):
+        qt = orc.rope(pt["q"].astype(np.float64), pos, out="f32")
+        kt = orc.rope(pt["k"].astype(np.float64), pos, out="f32")
+        orc.attention(qt, kt, pt["v"].astype(np.float64), orc.attention_mask(pos, wt.T), wt.attn_mult, wt.softcap)
+    t1 = (time.perf_counter() - t0) / 5
+    extra[wt.name] = {"ms": round(t1 * 1e3, 3), "cores": 1, "full": True, "unit": "TFLOP/s",
+                      "value": 4 * wt.D * wt.Hq * wt.T * (wt.T + 1) // 2 / t1 / 1e12}
+    for name in ("decode_b1_t8192", "decode_ragged_b32_t8192"):
+        wd = gi.WORKLOADS[name]
+        pd = gi.make_workload(name)
+        dtasks = [(pd["k_cache"][b:b + 1], pd["v_cache"][b:b + 1], pd["q"][b:b + 1], pd["k_new"][b:b + 1],
+                   pd["v_new"][b:b + 1], pd["step"][b:b + 1]) for b in range(wd.B)]
+        nw = min(workers, wd.B)
+        s = _timed_pool(name, _oracle_decode_seq, dtasks, nw)
+        L = pd["kv_len"].astype(np.int64)
+        del pd, dtasks
+        nbytes = int(L.sum()) * wd.Hkv * wd.D * 4 + wd.B * (2 * wd.Hq * wd.D * 2 + 2 * wd.Hkv * wd.D * 2)
+        extra[name] = {"ms": round(s * 1e3, 1), "cores": nw, "full": True, "value": nbytes / s / 1e9,
+                       "unit": "GB/s"}
+    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"{len(rows)} of {T} query rows (all 48 heads) of the 8k prefill, RoPE of q included "
+                      f"(keys rotated once per worker, untimed); {flop} flop in {sec:.1f} s on {workers} "
+                      f"single-threaded NumPy worker processes",
+            "other_workloads": extra}
 
 
 def main():
@@ -300,15 +392,19 @@ def main():
               "(the attention core shards with no exchange over KV heads: see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    cpu = None
+    if not args.no_cpu_baseline:  # before this process initialises the GPU
+        cpu = cpu_baseline()
+        print(f"# cpu baseline done: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} cores", file=sys.stderr,
+              flush=True)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import gqa_attention_grok_amd as grok
     import gqa_attention_grok_amd.pipeline as pipe
     import gqa_inputs as gi
-    import gpu_util as U
+    import gqa_inputs.device as U
 
     only = set(args.only.split(",")) if args.only else {"prefill", "decode_b1", "decode_ragged", "sublayer",
                                                         "decode_sublayer_b1", "decode_sublayer_b32", "chunk", "moe"}
@@ -380,9 +476,8 @@ def main():
             "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": tr, "kernel_ms": round(head["kernel_ms"], 4),
         }
-    if not args.no_cpu_baseline:
-        import oracle as orc
-        line["cpu_baseline"] = cpu_baseline(gi, orc)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     line["secondary"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                          for k, r in res.items() if r is not head}
     print(json.dumps(line), flush=True)

@@ -3,20 +3,12 @@ import numpy as np
 import torch
 
 import oracle as orc
+from gqa_inputs.device import dev, dev_bf16  # noqa: F401  (re-exported for the tests)
 
 # Tolerances stated for the hot path: bf16 outputs pass element-wise when
 # |gpu - ref| <= BF16_ATOL + BF16_RTOL * |ref|; fp32 outputs within F32_ATOL.
 BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
 F32_ATOL = 1e-5
-
-
-def dev_bf16(bits: np.ndarray) -> torch.Tensor:
-    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
-    return torch.from_numpy(a).cuda().view(torch.bfloat16)
-
-
-def dev(a: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -39,9 +31,12 @@ REL_L2_MAX = 5e-3
 
 def assert_bf16_close(got, ref, what="", rel_l2_max=REL_L2_MAX, magnitude=None):
     """Element-wise |got - ref| <= BF16_ATOL + BF16_RTOL * magnitude, where the
-    magnitude is |ref| unless given (for a sum y = x + n the relative part of
-    the bound belongs to the magnitude of the rounded summand, see the
-    sub-layer test)."""
+    magnitude is |ref| unless given. For a residual output y = x + n the tests
+    pass max(|y|, |n|): n = norm(o) is rounded to bf16 before the add, as the
+    sandwich norm hands it on, so y carries one bf16 rounding of n, up to
+    2**-9 |n| (0.031 at |n| = 4 to 8), which exceeds 2e-2 + 1e-2 |y| where x
+    and n cancel. Where |n| <= |y| the bound is the unwidened one; the number
+    of elements that need the widening is printed."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -56,6 +51,10 @@ def assert_bf16_close(got, ref, what="", rel_l2_max=REL_L2_MAX, magnitude=None):
     if rel_l2_max is not None:
         r = rel_l2(got, ref)
         assert r <= rel_l2_max, f"{what}: relative L2 error {r:.3e} > {rel_l2_max}"
+    if magnitude is not None:
+        # elements that pass only because of the widened magnitude
+        n_wide = int(np.count_nonzero(err > BF16_ATOL + BF16_RTOL * np.abs(ref)))
+        print(f"{what}: {n_wide} of {err.size} elements within the bound only through max(|y|, |n|)")
     return float(err.max())
 
 

@@ -120,6 +120,35 @@ def test_prefill_b1_t8192_sampled(G):
     print(f"prefill sampled {len(rows)} rows x {Hq} heads, max abs err {max(errs):.2e}")
 
 
+def test_prefill_b1_t8192_two_heads_every_row(G):
+    """Every one of the 8192 query rows of two heads in different KV groups
+    (head 0 on KV head 0, head 47 on KV head 7) against the oracle: all 256
+    query tiles of the 8k prefill, at the launch the benchmark times."""
+    grok, pipe, U, torch = G
+    w = gi.WORKLOADS["prefill_b1_t8192"]
+    p = gi.make_workload(w.name)
+    step = pipe.PrefillStep(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), w.attn_mult,
+                            w.softcap)
+    out = step()
+    torch.cuda.synchronize()
+    T, Hq, Hkv, D = w.T, w.Hq, w.Hkv, w.D
+    G_ = Hq // Hkv
+    pos = np.arange(T)[None]
+    k = orc.rope(orc.bf16_bits_to_f64(p["k"]), pos, out="bf16")
+    v = orc.bf16_bits_to_f64(p["v"])
+    errs = []
+    for h in (0, Hq - 1):
+        g = h // G_
+        got = U.host(out[0, :, h * D:(h + 1) * D])
+        qh = orc.rope(orc.bf16_bits_to_f64(p["q"][:, :, h:h + 1]), pos, out="bf16")
+        for r0 in range(0, T, 512):
+            rows = np.arange(r0, r0 + 512)[None]
+            ref = orc.attention(qh[:, r0:r0 + 512], k[:, :, g:g + 1], v[:, :, g:g + 1],
+                                orc.attention_mask(rows, T), w.attn_mult, w.softcap)[0]
+            errs.append(U.assert_bf16_close(got[r0:r0 + 512], ref, f"prefill h={h} rows {r0}..{r0 + 511}"))
+    print(f"prefill 2 heads x {T} rows, max abs err {max(errs):.2e}")
+
+
 def test_sublayer_b4_t2048_sampled(G):
     grok, pipe, U, torch = G
     w = gi.WORKLOADS["sublayer_b4_t2048"]
