@@ -23,6 +23,7 @@ __all__ = [
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
     "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
+    "grok_attn_decode_append_noalloc", "grok_attn_decode_append_noalloc_max_bytes",
     "grok_attn_decode_workspace_bytes", "grok_moe_workspace_bytes", "grok_moe_interleave",
     "grok_moe_route", "grok_moe_ffn", "grok_prefill_qkv_workspace_bytes", "grok_prefill_qkv",
 ]
@@ -58,6 +59,9 @@ _PROTOS = {
     "grok_attn_prefill_chunk": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _p]),
     "grok_attn_decode_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i,
                                      _f, _f, _f, _p]),
+    "grok_attn_decode_append_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
+                                             _f, _f, _f, _p]),
+    "grok_attn_decode_append_noalloc_max_bytes": (_sz, []),
     "grok_moe_workspace_bytes": (_sz, [_i64, _i, _i, _i, _i]),
     "grok_prefill_qkv_workspace_bytes": (_sz, [_i, _i]),
     "grok_prefill_qkv": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _i,
@@ -315,6 +319,34 @@ def grok_attn_decode_append(q, k_new, v_new, k_cache, v_cache, step, out, worksp
                                        _ptr(step), _ptr(new_step), _ptr(q_out), _ptr(out), _ptr(workspace),
                                        ws_bytes, _ptr(status), B, Tmax, Hq, Hkv, D, attn_mult, softcap,
                                        rope_base, _stream(q)), "grok_attn_decode_append")
+    return out
+
+
+def grok_attn_decode_append_noalloc_max_bytes():
+    return int(lib.grok_attn_decode_append_noalloc_max_bytes())
+
+
+def grok_attn_decode_append_noalloc(q, k_new, v_new, k_cache, v_cache, step, out, attn_mult, softcap=30.0,
+                                    new_step=None, q_out=None, status=None, rope_base=10000.0):
+    """grok_attn_decode_append without a workspace: the library's per-GPU
+    scratch array holds the split partials (no device allocation per call;
+    calls that overlap on one GPU race)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_new, "k_new", torch.bfloat16, 4)
+    _need(v_new, "v_new", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(step, "step", torch.int32, 1)
+    _need(out, "out", torch.bfloat16)
+    _need(new_step, "new_step", torch.int32, 1)
+    _need(q_out, "q_out", torch.bfloat16)
+    _need(status, "status", torch.int32)
+    B, _, Hq, D = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(lib.grok_attn_decode_append_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                               _ptr(step), _ptr(new_step), _ptr(q_out), _ptr(out), _ptr(status),
+                                               B, Tmax, Hq, Hkv, D, attn_mult, softcap, rope_base, _stream(q)),
+           "grok_attn_decode_append_noalloc")
     return out
 
 

@@ -146,6 +146,10 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
                          void *out, void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,
                          float mult, float cap, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv);
+// Device scratch of the allocation-free decode entry point (decode.hip): its
+// size, and its device address on the current GPU (looked up once per GPU).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_static_scratch(void **ptr);
 hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, void *kc, void *vc,
                                 const int32_t *step, int32_t *new_step, void *q_out, void *out,
                                 void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,

@@ -36,9 +36,18 @@
 // both into the cache. The rotation is rope_rotate of common.h at the phases
 // of rope_phase, rounded to bf16 as the unfused append rounds it, so the
 // results are those of the separate append + decode calls.
+#include <mutex>
+
 #include "attn_tile.h"
 
 namespace grok {
+
+// Split-partial buffer of the allocation-free decode entry point: one copy per
+// GPU, held from the library's load on that GPU until the process ends. Host
+// code must not pass this name to a kernel (on the host it is a stand-in, not
+// a device address): decode_static_scratch() returns the device address.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
 namespace {
 
 using namespace attn;
@@ -352,6 +361,26 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
 }
 
 }  // namespace
+
+hipError_t decode_static_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *dev_ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    // once per device, with that device current: its own copy's address
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv) {
   const size_t S = (static_cast<size_t>(Tmax) + kSplit - 1) / kSplit;

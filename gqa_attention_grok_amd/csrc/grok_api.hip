@@ -257,38 +257,77 @@ int grok_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                     "attn_decode");
 }
 
+namespace {
+
+// Validation shared by the two decode-append entry points; 0 when fine.
+int decode_append_check(const char *who, const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                        const void *v_cache, const int32_t *step, const int32_t *new_step, const void *q_out,
+                        const void *out, int B, int Tmax, int Hq, int Hkv, int D, float attn_mult, float softcap,
+                        float rope_base) {
+  if (B < 1 || Tmax < 1 || Hq < 1 || Hkv < 1) return fail(GROK_EINVAL, "%s: bad shape", who);
+  if (Hq % Hkv) return fail(GROK_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", who, Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(GROK_EINVAL, "%s: at most 16 query heads per KV head", who);
+  if (D != 128) return fail(GROK_EINVAL, "%s: head size must be 128 (D=%d)", who, D);
+  if (bad_softmax_params(attn_mult, softcap))
+    return fail(GROK_EINVAL, "%s: attn_mult must be finite and softcap in (0, 40]", who);
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return fail(GROK_EINVAL, "%s: bad rope_base", who);
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !step || !out) return fail(GROK_EINVAL, "%s: null pointer", who);
+  if (new_step && new_step == step) return fail(GROK_EINVAL, "%s: new_step must not alias step", who);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
+                       reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
+                       reinterpret_cast<uintptr_t>(q_out);
+  if (al % 16) return fail(GROK_EINVAL, "%s: misaligned pointer", who);
+  if (overlaps(q, static_cast<size_t>(B) * Hq * D * 2, q_out, static_cast<size_t>(B) * Hq * D * 2))
+    return fail(GROK_EINVAL, "%s: q_out overlaps q", who);
+  if (static_cast<int64_t>(B) * Hq > 0x7fffffff || B > 65535) return fail(GROK_EINVAL, "%s: batch too large", who);
+  return 0;
+}
+
+}  // namespace
+
 int grok_attn_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
                             void *v_cache, const int32_t *step, int32_t *new_step, void *q_out,
                             void *out, void *workspace, size_t ws_bytes, int32_t *status, int B,
                             int Tmax, int Hq, int Hkv, int D, float attn_mult, float softcap,
                             float rope_base, hipStream_t stream) {
-  if (B < 1 || Tmax < 1 || Hq < 1 || Hkv < 1) return fail(GROK_EINVAL, "attn_decode_append: bad shape");
-  if (Hq % Hkv) return fail(GROK_EINVAL, "attn_decode_append: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
-  if (Hq / Hkv > 16) return fail(GROK_EINVAL, "attn_decode_append: at most 16 query heads per KV head");
-  if (D != 128) return fail(GROK_EINVAL, "attn_decode_append: head size must be 128 (D=%d)", D);
-  if (bad_softmax_params(attn_mult, softcap))
-    return fail(GROK_EINVAL, "attn_decode_append: attn_mult must be finite and softcap in (0, 40]");
-  if (!(rope_base > 0.f) || !isfinite(rope_base)) return fail(GROK_EINVAL, "attn_decode_append: bad rope_base");
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !step || !out || !workspace)
-    return fail(GROK_EINVAL, "attn_decode_append: null pointer");
-  if (new_step && new_step == step) return fail(GROK_EINVAL, "attn_decode_append: new_step must not alias step");
-  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
-                       reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
-                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
-                       reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(workspace);
-  if (al % 16) return fail(GROK_EINVAL, "attn_decode_append: misaligned pointer");
-  if (overlaps(q, static_cast<size_t>(B) * Hq * D * 2, q_out, static_cast<size_t>(B) * Hq * D * 2))
-    return fail(GROK_EINVAL, "attn_decode_append: q_out overlaps q");
+  if (int r = decode_append_check("attn_decode_append", q, k_new, v_new, k_cache, v_cache, step, new_step, q_out,
+                                  out, B, Tmax, Hq, Hkv, D, attn_mult, softcap, rope_base))
+    return r;
+  if (!workspace) return fail(GROK_EINVAL, "attn_decode_append: null workspace");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(GROK_EINVAL, "attn_decode_append: misaligned pointer");
   const size_t need = grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);
   if (ws_bytes < need)
     return fail(GROK_ENOMEM, "attn_decode_append: workspace %zu bytes < %zu needed", ws_bytes, need);
-  if (static_cast<int64_t>(B) * Hq > 0x7fffffff || B > 65535) return fail(GROK_EINVAL, "attn_decode_append: batch too large");
   grok::RopeFreqs f;
   grok::rope_build_freqs(D, rope_base, &f);
   return hip_status(grok::launch_decode_append(q, k_new, v_new, k_cache, v_cache, step, new_step, q_out, out,
                                                workspace, status, B, Tmax, Hq, Hkv, attn_mult, softcap, f,
                                                stream),
                     "attn_decode_append");
+}
+
+size_t grok_attn_decode_append_noalloc_max_bytes(void) { return grok::kDecodeScratchBytes; }
+
+int grok_attn_decode_append_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                                    void *v_cache, const int32_t *step, int32_t *new_step, void *q_out,
+                                    void *out, int32_t *status, int B, int Tmax, int Hq, int Hkv, int D,
+                                    float attn_mult, float softcap, float rope_base, hipStream_t stream) {
+  if (int r = decode_append_check("attn_decode_append_noalloc", q, k_new, v_new, k_cache, v_cache, step, new_step,
+                                  q_out, out, B, Tmax, Hq, Hkv, D, attn_mult, softcap, rope_base))
+    return r;
+  const size_t need = grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);
+  if (need > grok::kDecodeScratchBytes)
+    return fail(GROK_ENOMEM, "attn_decode_append_noalloc: these sizes need %zu bytes of scratch, above the "
+                "%zu-byte maximum (use grok_attn_decode_append with a workspace)", need, grok::kDecodeScratchBytes);
+  void *ws = nullptr;
+  hipError_t e = grok::decode_static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "attn_decode_append_noalloc: scratch lookup");
+  grok::RopeFreqs f;
+  grok::rope_build_freqs(D, rope_base, &f);
+  return hip_status(grok::launch_decode_append(q, k_new, v_new, k_cache, v_cache, step, new_step, q_out, out, ws,
+                                               status, B, Tmax, Hq, Hkv, attn_mult, softcap, f, stream),
+                    "attn_decode_append_noalloc");
 }
 
 int grok_attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache,

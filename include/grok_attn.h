@@ -12,8 +12,9 @@
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers (HIP global memory), row-major and
  *   contiguous, owned by the caller. The library allocates nothing, keeps no
- *   state between calls, and never synchronises: work is enqueued on `stream`
- *   (NULL = the default stream) and the call returns.
+ *   state between calls (one exception: the per-GPU scratch array of
+ *   grok_attn_decode_append_noalloc), and never synchronises: work is
+ *   enqueued on `stream` (NULL = the default stream) and the call returns.
  * - Return value: GROK_OK (0) or a negative GROK_E* code. Arguments are
  *   validated on the host before anything is enqueued; on an error nothing is
  *   enqueued and grok_last_error() (thread-local) describes the problem.
@@ -298,6 +299,30 @@ GROK_API int grok_attn_decode_append(const void *q, const void *k_new, const voi
                                      size_t ws_bytes, int32_t *status, int B, int Tmax, int Hq,
                                      int Hkv, int D, float attn_mult, float softcap,
                                      float rope_base, hipStream_t stream);
+
+/*
+ * grok_attn_decode_append without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid it. Same arguments,
+ * kernels, results (bit for bit) and errors as grok_attn_decode_append; the
+ * split partial sums go to a device array inside the library instead, one
+ * copy per GPU of grok_attn_decode_append_noalloc_max_bytes() (64 MiB) bytes,
+ * held from the first call on that GPU until the process ends. Its address
+ * is looked up on the first call on each GPU; no call allocates.
+ * Limit: grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D) must not
+ * exceed that maximum (at 48/8 heads: B * ceil(Tmax/128) <= 2709, e.g. 42
+ * sequences of an 8192-slot cache), else ENOMEM and nothing is enqueued.
+ * All calls on one GPU share the array and its contents persist between
+ * calls (they need no initialisation): calls that may overlap in time on
+ * one GPU (other streams, other host threads) race and must not be issued.
+ */
+GROK_API size_t grok_attn_decode_append_noalloc_max_bytes(void);
+GROK_API int grok_attn_decode_append_noalloc(const void *q, const void *k_new, const void *v_new,
+                                             void *k_cache, void *v_cache, const int32_t *step,
+                                             int32_t *new_step, void *q_out, void *out,
+                                             int32_t *status, int B, int Tmax, int Hq, int Hkv, int D,
+                                             float attn_mult, float softcap, float rope_base,
+                                             hipStream_t stream);
 
 /* Workspace bytes grok_attn_decode needs for these sizes (0 on bad sizes). */
 GROK_API size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D);

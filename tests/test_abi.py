@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 22, syms
+    assert len(syms) == 24, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -254,6 +254,26 @@ def test_decode_append_validation(lib):
     assert call(q_out=ctypes.c_void_p(0x10008)) == EINVAL
     assert call(q_out=FAKE) == EINVAL and "overlaps q" in _err(lib)       # split 0 writes q_out while others read q
     assert call(q_out=ctypes.c_void_p(0x10000 + 48 * 256 - 16)) == EINVAL  # partial overlap
+
+
+def test_decode_append_noalloc_validation(lib):
+    mx = lib.grok_attn_decode_append_noalloc_max_bytes
+    mx.restype = ctypes.c_size_t
+    assert mx() == 64 << 20
+    f = lib.grok_attn_decode_append_noalloc
+    f.restype = ctypes.c_int
+
+    def call(B=1, Tmax=8192, Hq=48, Hkv=8, D=128, cap=30.0, q=FAKE, new_step=None, q_out=None):
+        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, new_step, q_out, FAKE, None, i(B), i(Tmax), i(Hq), i(Hkv), i(D),
+                 fl(0.088), fl(cap), fl(1e4), None)
+    # 43 sequences of 8192 slots need 43*64 splits of 24768 bytes: above the 64 MiB array
+    assert call(B=43) == ENOMEM and "maximum" in _err(lib)
+    assert call(B=1, Tmax=8192 * 43) == ENOMEM
+    assert call(D=64) == EINVAL
+    assert call(cap=45.0) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(new_step=FAKE) == EINVAL          # aliases step
+    assert call(q_out=FAKE) == EINVAL             # overlaps q
 
 
 def test_prefill_chunk_validation(lib):
