@@ -208,14 +208,23 @@ def bench_decode_sublayer(torch, grok, pipe, U, gi, name, steps, warmup, replica
     nbytes = w_bytes + kv_bytes + io_bytes
     sec = time_steps(torch, pipe, steps_obj, steps, warmup)
 
-    # the weight-streaming kernels of one step (norm + Q|K|V + RoPE + append, and
-    # the output projection), replayed from graphs (no host work)
-    proj_ms = time_steps(torch, pipe, [lambda s_=s_: (s_.front(), s_.project_out()) for s_ in steps_obj],
+    # the weight-streaming kernels of one step (norm + Q|K|V + RoPE + append;
+    # the output projection with the post-norm and residual), replayed from
+    # graphs (no host work)
+    proj_ms = time_steps(torch, pipe, [lambda s_=s_: (s_.front(), s_.back()) for s_ in steps_obj],
                          steps, warmup) * 1e3
-    pbytes = d * cols + Hq * D * d + 4 * (cols + d) + B * 2 * (d + cols + Hq * D + d)
+    # weights and scales once; x in, q and the k/v rows out; attn and x in, y out
+    pbytes = d * cols + Hq * D * d + 4 * (cols + d) + B * 2 * (d + cols + Hq * D + 2 * d)
+    # the same step with the back half as the separate projection and norm
+    ref_obj = [pipe.DecodeSublayerStep(s_.x, s_.k_cache, s_.v_cache, s_.step, *s_.w_args, s_.Hq, s_.Hkv, s_.D,
+                                       s_.attn_mult, s_.softcap, s_.eps, fused_back=False) for s_ in steps_obj]
+    sec_unfused_back = time_steps(torch, pipe, ref_obj, steps, warmup)
+    del ref_obj
     return {
         "workload": name, "ms_per_step": sec * 1e3, "value": nbytes / sec / 1e9, "unit": "GB/s",
-        "bytes_per_step": nbytes, "kernel": "decode_qkv_kernel + gemv_packed_kernel (Q|K|V with norm/RoPE/append, O)",
+        "ms_per_step_back_half_unfused": sec_unfused_back * 1e3,
+        "bytes_per_step": nbytes,
+        "kernel": "decode_qkv_kernel + gemv_out_norm_kernel (Q|K|V with norm/RoPE/append; O with norm and residual)",
         "kernel_ms": proj_ms, "kernel_gbs": pbytes / (proj_ms * 1e-3) / 1e9,
         "kernel_frac_of_hbm_peak": pbytes / (proj_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "replicas": replicas,

@@ -21,7 +21,8 @@ __all__ = [
     "GrokError", "LIB_PATH", "lib", "GROK_BF16", "GROK_F32",
     "grok_abi_version", "grok_status_string", "grok_last_error",
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
-    "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_rope", "grok_kv_append",
+    "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_decode_out",
+    "grok_decode_out_workspace_bytes", "grok_rope", "grok_kv_append",
     "grok_attn_prefill", "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
     "grok_attn_decode_append_noalloc", "grok_attn_decode_append_noalloc_max_bytes",
     "grok_attn_decode_workspace_bytes", "grok_moe_workspace_bytes", "grok_moe_interleave",
@@ -51,6 +52,8 @@ _PROTOS = {
     "grok_linear_int8_gemv": (_i, [_p, _i, _p, _p, _p, _p, _i64, _i, _p]),
     "grok_decode_qkv": (_i, [_p, _p, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                              _i, _i, _i, _i, _i, _i, _f, _p]),
+    "grok_decode_out_workspace_bytes": (_sz, [_i, _i, _i]),
+    "grok_decode_out": (_i, [_p, _p, _p, _p, _f, _p, _p, _p, _sz, _i, _i, _i, _p]),
     "grok_rope": (_i, [_p, _i, _i, _i, _i, _p, _f, _i, _p]),
     "grok_kv_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
@@ -240,6 +243,31 @@ def grok_rope(x, offset=None, base=10000.0):
     _check(lib.grok_rope(_ptr(x), B, T, H, D, _ptr(offset), base, _dtype_code(x), _stream(x)),
            "grok_rope")
     return x
+
+
+def grok_decode_out_workspace_bytes(B, d_in, d_out):
+    return int(lib.grok_decode_out_workspace_bytes(B, d_in, d_out))
+
+
+def grok_decode_out(attn, wo_packed, so, residual, y, workspace, gamma=None, eps=1e-5):
+    """y = residual + norm(attn @ (Wo * so)) for one token per sequence (the
+    attention sub-layer's back half); one launch for up to 4 rows. The
+    workspace (uint8, grok_decode_out_workspace_bytes) must be zeroed once
+    before its first use; each call leaves it ready for the next."""
+    _need(attn, "attn", torch.bfloat16)
+    _need(wo_packed, "wo_packed", torch.int8)
+    _need(so, "so", torch.float32, 1)
+    _need(gamma, "gamma", torch.float32, 1)
+    _need(residual, "residual", torch.bfloat16)
+    _need(y, "y", torch.bfloat16)
+    _need(workspace, "workspace")
+    d_out = so.shape[0]
+    B = residual.numel() // d_out
+    d_in = attn.numel() // B
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.grok_decode_out(_ptr(attn), _ptr(wo_packed), _ptr(so), _ptr(gamma), eps, _ptr(residual), _ptr(y),
+                               _ptr(workspace), ws_bytes, B, d_in, d_out, _stream(attn)), "grok_decode_out")
+    return y
 
 
 def grok_kv_append(k_cache, v_cache, k_new, v_new, step, q_inout=None, new_step=None,

@@ -125,6 +125,14 @@ hipError_t launch_linear_int8_pack(const int8_t *w, int8_t *wp, int K, int N, hi
 hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
                                    const float *const *scales, void *const *y, const int *N,
                                    int64_t M, int K, hipStream_t s);
+// Output projection + post-norm + residual for few rows (linear_int8_gemv.hip):
+// one launch for up to out_norm_max_fused_rows(K) rows, else the projection
+// and grok_rmsnorm's kernel. The workspace holds an arrival counter (zero
+// between calls), per-workgroup sums of squares and the bf16 projection.
+size_t out_norm_workspace_bytes(int64_t M, int N);
+int out_norm_max_fused_rows(int K);
+hipError_t launch_out_norm(const void *x, const int8_t *w, const float *scale, const float *gamma, float eps,
+                           const void *res, void *y, void *ws, int64_t M, int K, int N, hipStream_t stream);
 // Decode front half: [norm] -> Q|K|V (packed weights) -> RoPE -> cache slot.
 hipError_t launch_decode_qkv(const void *x, const float *gamma, float eps, bool prenorm,
                              const int8_t *const *w, const float *const *scales, void *q_out,

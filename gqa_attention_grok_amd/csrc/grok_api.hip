@@ -168,6 +168,35 @@ int grok_decode_qkv(const void *x, const float *gamma, float eps, int prenorm,
                     "decode_qkv");
 }
 
+size_t grok_decode_out_workspace_bytes(int B, int d_in, int d_out) {
+  if (B < 1 || d_in < 8 || d_in % 8 || d_out < 8 || d_out % 8) return 0;
+  return grok::out_norm_workspace_bytes(B, d_out);
+}
+
+int grok_decode_out(const void *attn, const int8_t *wo_packed, const float *so, const float *gamma, float eps,
+                    const void *residual, void *y, void *workspace, size_t ws_bytes, int B, int d_in, int d_out,
+                    hipStream_t stream) {
+  if (B < 1 || d_in < 8 || d_in % 8 || d_out < 8 || d_out % 8)
+    return fail(GROK_EINVAL, "decode_out: bad shape B=%d d_in=%d d_out=%d (positive multiples of 8)", B, d_in, d_out);
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(GROK_EINVAL, "decode_out: bad eps");
+  if (!attn || !wo_packed || !so || !residual || !y || !workspace) return fail(GROK_EINVAL, "decode_out: null pointer");
+  const uintptr_t a16 = reinterpret_cast<uintptr_t>(attn) | reinterpret_cast<uintptr_t>(wo_packed) |
+                        reinterpret_cast<uintptr_t>(residual) | reinterpret_cast<uintptr_t>(y) |
+                        reinterpret_cast<uintptr_t>(workspace);
+  const uintptr_t a4 = reinterpret_cast<uintptr_t>(so) | reinterpret_cast<uintptr_t>(gamma);
+  if (a16 % 16 || a4 % 4) return fail(GROK_EINVAL, "decode_out: misaligned pointer");
+  const size_t need = grok::out_norm_workspace_bytes(B, d_out);
+  if (ws_bytes < need) return fail(GROK_ENOMEM, "decode_out: workspace %zu bytes < %zu needed", ws_bytes, need);
+  const size_t ny = static_cast<size_t>(B) * d_out * 2;
+  if (overlaps(y, ny, attn, static_cast<size_t>(B) * d_in * 2) || overlaps(y, ny, workspace, need) ||
+      overlaps(attn, static_cast<size_t>(B) * d_in * 2, workspace, need) ||
+      overlaps(residual, ny, workspace, need))
+    return fail(GROK_EINVAL, "decode_out: y, attn or residual overlaps the workspace, or y overlaps attn");
+  return hip_status(grok::launch_out_norm(attn, wo_packed, so, gamma, eps, residual, y, workspace, B, d_in, d_out,
+                                          stream),
+                    "decode_out");
+}
+
 int grok_rope(void *x, int B, int T, int H, int D, const int32_t *offset, float base, int dtype,
               hipStream_t stream) {
   if (dtype != GROK_BF16 && dtype != GROK_F32) return fail(GROK_EINVAL, "rope: unknown dtype %d", dtype);

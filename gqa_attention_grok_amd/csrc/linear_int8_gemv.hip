@@ -476,6 +476,162 @@ __global__ __launch_bounds__(kThreads) void decode_qkv_kernel(QkvArgs qa) {
   }
 }
 
+// Output projection with the sandwich post-norm and the residual add in one
+// launch (ch. 6 "model.py close reading, part 3", §6.3.1: h = x + norm(o),
+// o = attn @ (Wo * s), ch. 4 §4.1), for at most 4 rows held in LDS:
+//   o = bf16(attn @ (w * s)),  r_m = rsqrt(mean_n(o_mn^2) + eps),
+//   y = bf16(res + bf16(gamma * (o * r_m)))
+// with the roundings of grok_linear_int8_gemv followed by grok_rmsnorm. The
+// norm needs every channel of a row, and each workgroup owns 16 channels, so
+// the workgroups meet through memory: each writes its bf16 o values and its
+// rows' sums of squares with device-coherent stores, waits until they are
+// written, and counts itself in with a device-scope atomic add; the last one
+// to arrive reads everything back with device-coherent loads, sums the
+// squares in workgroup order (so the result does not depend on the arrival
+// order), normalises, adds the residual and writes y. It also puts the
+// counter back to zero, so each call leaves it as it found it.
+struct OutNormArgs {
+  GemvArgs g;          // mat[0]: the packed Wo, y = the o buffer of the workspace
+  const bf16_t *res;   // [M][N]
+  bf16_t *out;         // [M][N]
+  const float *gamma;  // [N] or NULL (unit scale)
+  float eps;
+  float *ss;           // [workgroups][4] sums of squares of o
+  uint32_t *count;     // arrivals; zero between calls
+};
+
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kOutPieces = 6;  // 16-byte pieces of o per thread held in registers (4 rows of 6144)
+
+__global__ __launch_bounds__(kThreads) void gemv_out_norm_kernel(OutNormArgs na) {
+  constexpr int MT = 1, NB = 1, D = 16;
+  extern __shared__ f32x4 xs4[];  // attn rows [M][K] bf16
+  __shared__ float red[kWaves][4][kTileCols];
+  __shared__ float rsum[kWaves][4];
+  __shared__ int last;
+  const GemvArgs &a = na.g;
+  const int tid = threadIdx.x;
+  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
+  const int M = a.M, K = a.K, KP = a.KP, N = a.mat[0].N;
+  const int j0 = blockIdx.x;
+
+  TileRing<MT, NB, D, true> ring;
+  ring.i0 = static_cast<int>(static_cast<int64_t>(KP) * wv / kWaves);
+  ring.i1 = static_cast<int>(static_cast<int64_t>(KP) * (wv + 1) / kWaves);
+  ring.K = K;
+  ring.M = M;
+  ring.g = g;
+  ring.i16 = i16;
+  ring.wb[0] = a.mat[0].w + (static_cast<int64_t>(j0) * KP) * kTileBytes + 16 * l;
+  ring.xr[0] = a.x;
+  XStage xst;
+  xst.load(a.x, M * K / 8);
+  ring.prologue();
+  bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
+  xst.template store<D * TileRing<MT, NB, D, true>::kLoads, false>(xs, ring.busy(), M, K, nullptr, 0.f,
+                                                                    &red[0][0][0]);
+  f32x4 acc[NB][MT];
+  ring.run(xs, acc);
+
+  __syncthreads();  // red[] may have held the staging sums
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (4 * g + e < M) red[wv][4 * g + e][i16] = acc[0][0][e];
+  __syncthreads();
+  // wave 0, lane 16m + c: channel 16*j0 + c of row m
+  if (wv == 0) {
+    const int m = g, n = kTileCols * j0 + i16;
+    float sq = 0.f;
+    if (m < M && n < N) {
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kWaves; ++u) sum += red[u][m][i16];
+      const bf16_t o = f32_to_bf16(sum * a.mat[0].s[n]);
+      __hip_atomic_store(a.mat[0].y + static_cast<int64_t>(m) * N + n, o, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      const float of = bf16_to_f32(o);
+      sq = of * of;
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+    if (i16 == 0 && m < M)
+      __hip_atomic_store(na.ss + 4 * j0 + m, sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are written
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(na.count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+
+  // The last workgroup: every o value and sum of squares has been written.
+  // Its loads all go out before the first use (one memory round trip): the
+  // thread's pieces of o, the residual and gamma, then the sums of squares.
+  if (tid == 0) __hip_atomic_store(na.count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int n8 = M * N / 8;  // 8 values (16 bytes) per piece; a piece lies in one row (N % 8 == 0)
+  u32x4 ow[kOutPieces], xw[kOutPieces];
+#pragma unroll
+  for (int u = 0; u < kOutPieces; ++u) {
+    const int c = tid + u * kThreads;
+    if (c < n8) {
+      const uint32_t *op = reinterpret_cast<const uint32_t *>(a.mat[0].y + 8 * static_cast<int64_t>(c));
+      ow[u] = u32x4{coherent_load(op), coherent_load(op + 1), coherent_load(op + 2), coherent_load(op + 3)};
+      xw[u] = *reinterpret_cast<const u32x4 *>(na.res + 8 * static_cast<int64_t>(c));
+    }
+  }
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int w = tid; w < static_cast<int>(gridDim.x); w += kThreads)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (m < M) part[m] += __uint_as_float(coherent_load(reinterpret_cast<const uint32_t *>(na.ss + 4 * w + m)));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float v = wave_sum(part[m]);
+    if (l == 0) rsum[wv][m] = v;
+  }
+  __syncthreads();
+  float r[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) t += rsum[u][m];
+    r[m] = rsqrtf(t / static_cast<float>(N) + na.eps);
+  }
+  auto finish = [&](int c, const u32x4 &o4, const u32x4 &x4) {
+    const int m = 8 * c / N, n0 = 8 * c - m * N;
+    const float rm = m == 0 ? r[0] : m == 1 ? r[1] : m == 2 ? r[2] : r[3];
+    u32x4 yw;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float f0 = lo_bf16(o4[q]) * rm, f1 = hi_bf16(o4[q]) * rm;
+      if (na.gamma) {
+        f0 = na.gamma[n0 + 2 * q] * f0;
+        f1 = na.gamma[n0 + 2 * q + 1] * f1;
+      }
+      f0 = lo_bf16(x4[q]) + bf16_to_f32(f32_to_bf16(f0));
+      f1 = hi_bf16(x4[q]) + bf16_to_f32(f32_to_bf16(f1));
+      yw[q] = pack_bf16x2(f0, f1);
+    }
+    *reinterpret_cast<u32x4 *>(na.out + 8 * static_cast<int64_t>(c)) = yw;
+  };
+#pragma unroll
+  for (int u = 0; u < kOutPieces; ++u) {
+    const int c = tid + u * kThreads;
+    if (c < n8) finish(c, ow[u], xw[u]);
+  }
+  for (int c = tid + kOutPieces * kThreads; c < n8; c += kThreads) {  // rows wider than the registers hold
+    const uint32_t *op = reinterpret_cast<const uint32_t *>(a.mat[0].y + 8 * static_cast<int64_t>(c));
+    finish(c, u32x4{coherent_load(op), coherent_load(op + 1), coherent_load(op + 2), coherent_load(op + 3)},
+           *reinterpret_cast<const u32x4 *>(na.res + 8 * static_cast<int64_t>(c)));
+  }
+}
+
 // Packing: one thread per 16-byte lane chunk of a tile.
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t *w, int8_t *wp, int K, int N, int KP,
                                                    int64_t chunks) {
@@ -552,6 +708,50 @@ hipError_t launch_linear_int8_gemv(const void *x, int n, const int8_t *const *w,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+size_t out_norm_workspace_bytes(int64_t M, int N) {
+  const size_t nwg = static_cast<size_t>((N + kTileCols - 1) / kTileCols);
+  const size_t ss = (nwg * 4 * sizeof(float) + 255) / 256 * 256;
+  return 256 + ss + static_cast<size_t>(M) * N * 2;
+}
+
+int out_norm_max_fused_rows(int K) { return K > 0 ? (kStageElems / K < 4 ? kStageElems / K : 4) : 0; }
+
+hipError_t launch_out_norm(const void *x, const int8_t *w, const float *scale, const float *gamma, float eps,
+                           const void *res, void *y, void *ws, int64_t M, int K, int N, hipStream_t stream) {
+  unsigned char *wsb = static_cast<unsigned char *>(ws);
+  const size_t nwg = static_cast<size_t>((N + kTileCols - 1) / kTileCols);
+  uint32_t *count = reinterpret_cast<uint32_t *>(wsb);
+  float *ss = reinterpret_cast<float *>(wsb + 256);
+  bf16_t *o = reinterpret_cast<bf16_t *>(wsb + 256 + (nwg * 4 * sizeof(float) + 255) / 256 * 256);
+  if (M > out_norm_max_fused_rows(K)) {
+    // more rows than the fused form keeps on chip: the projection, then the norm
+    const int8_t *wp[1] = {w};
+    const float *sp[1] = {scale};
+    void *yp[1] = {o};
+    const int Np[1] = {N};
+    hipError_t e = launch_linear_int8_gemv(x, 1, wp, sp, yp, Np, M, K, stream);
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm(o, gamma, res, y, M, N, eps, GROK_BF16, stream);
+  }
+  OutNormArgs na = {};
+  GemvArgs &a = na.g;
+  a.x = static_cast<const bf16_t *>(x);
+  a.mat[0] = GemvMat{w, scale, o, N, 0};
+  a.nmat = 1;
+  a.M = static_cast<int>(M);
+  a.K = K;
+  a.KP = (K + kTileRows - 1) / kTileRows;
+  na.res = static_cast<const bf16_t *>(res);
+  na.out = static_cast<bf16_t *>(y);
+  na.gamma = gamma;
+  na.eps = eps;
+  na.ss = ss;
+  na.count = count;
+  const size_t lds = static_cast<size_t>(M) * K * 2;
+  hipLaunchKernelGGL(gemv_out_norm_kernel, dim3(static_cast<unsigned>(nwg)), dim3(kThreads), lds, stream, na);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_qkv(const void *x, const float *gamma, float eps, bool prenorm,

@@ -30,7 +30,7 @@ import torch
 
 from . import (grok_attn_decode, grok_attn_decode_append, grok_attn_decode_workspace_bytes,
                grok_attn_prefill, grok_attn_prefill_chunk,
-               grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
+               grok_decode_out, grok_decode_out_workspace_bytes, grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
                grok_linear_int8_pack, grok_moe_ffn, grok_moe_interleave, grok_moe_workspace_bytes,
                grok_prefill_qkv, grok_prefill_qkv_workspace_bytes, grok_rmsnorm, grok_rope)
 
@@ -187,17 +187,21 @@ class DecodeSublayerStep:
     """Attention sub-layer for one new token per sequence, with KV memory:
     n = norm(x); q, k, v = n . W (one launch for the three); RoPE q and k at
     step[b] and append k, v at slot step[b]; decode attention over slots
-    [0, step[b]+1); y = x + norm(attn . Wo). x [B, 1, d]; the caches are
+    [0, step[b]+1); y = x + norm(attn . Wo) (one launch with fused=True). x
+    [B, 1, d]; the caches are
     updated in place, the step counter is not advanced (kv_len = step + 1).
     The int8 weights are repacked once, here, into the layout the few-row
     product streams."""
 
     def __init__(self, x, k_cache, v_cache, step, wq, sq, wk, sk, wv, sv, wo, so, Hq, Hkv, D,
-                 attn_mult, softcap=30.0, eps=1e-5, rope_base=10000.0, fused=True):
+                 attn_mult, softcap=30.0, eps=1e-5, rope_base=10000.0, fused=True, fused_back=None):
         self.x, self.k_cache, self.v_cache, self.step = x, k_cache, v_cache, step
         self.fused = fused
+        self.fused_back = fused if fused_back is None else fused_back
         # the fused pre-norm keeps x on chip: up to 4 rows of up to 8192 values in all
         self.max_prenorm_rows = min(4, 32768 // x.shape[-1])
+        self.w_args = (wq, sq, wk, sk, wv, sv, wo, so)
+        self.Hq, self.Hkv, self.D = Hq, Hkv, D
         self.packed = tuple(grok_linear_int8_pack(w_) for w_ in (wq, wk, wv, wo))
         self.scales = (sq, sk, sv, so)
         self.attn_mult, self.softcap, self.eps, self.rope_base = attn_mult, softcap, eps, rope_base
@@ -216,6 +220,8 @@ class DecodeSublayerStep:
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         nbytes = grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D)
         self.attn_ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        # zeroed once: the back half's arrival counter is left at zero by every call
+        self.out_ws = torch.zeros(grok_decode_out_workspace_bytes(B, Hq * D, d), dtype=torch.uint8, device=dev)
 
     def project_qkv(self):
         pq, pk, pv, _ = self.packed
@@ -224,6 +230,15 @@ class DecodeSublayerStep:
 
     def project_out(self):
         grok_linear_int8_gemv(self.attn, [self.packed[3]], [self.scales[3]], [self.o])
+
+    def back(self):
+        """output projection -> post-norm -> + x. Fused: one launch (for up to
+        4 rows; two inside the call for more); unfused: projection, norm."""
+        if self.fused_back:
+            grok_decode_out(self.attn, self.packed[3], self.scales[3], self.x, self.y, self.out_ws, eps=self.eps)
+        else:
+            self.project_out()
+            grok_rmsnorm(self.o, self.y, residual=self.x, eps=self.eps)
 
     def front(self):
         """norm -> Q|K|V -> RoPE -> cache slot. Fused into one launch (the norm
@@ -248,8 +263,7 @@ class DecodeSublayerStep:
         self.front()
         grok_attn_decode(self.q, self.k_cache, self.v_cache, self.kv_len, self.attn, self.attn_ws,
                          self.attn_mult, self.softcap, status=self.status)
-        self.project_out()
-        grok_rmsnorm(self.o, self.y, residual=self.x, eps=self.eps)
+        self.back()
         return self.y
 
 

@@ -161,6 +161,36 @@ GROK_API int grok_decode_qkv(const void *x, const float *gamma, float eps, int p
                              int Hkv, int D, float rope_base, hipStream_t stream);
 
 /*
+ * Back half of the attention sub-layer for one token per sequence ([ch4]
+ * §4.1 int8 Linear, §4.5.4 output projection; [ch6] §6.3.1 sandwich norm
+ * and residual): with o = bf16(attn[b] @ (Wo * so)),
+ *   y[b] = bf16(residual[b] + bf16(gamma * o * rsqrt(mean(o^2) + eps)))
+ * with the roundings (and, for a given o, the arithmetic) of
+ * grok_linear_int8_gemv followed by grok_rmsnorm with the residual; the sum
+ * of squares is taken in another order, so y may differ from those calls by
+ * one bf16 rounding. Up to 4 rows (of d_in <= 8192) run as one launch: the
+ * workgroups, 16 output channels each, meet through the workspace and the
+ * last one to finish normalises and adds the residual. More rows run the
+ * projection and the norm as two launches.
+ *   attn     [B, d_in] bf16;  wo_packed  grok_linear_int8_pack of Wo [d_in, d_out];
+ *   so       [d_out] fp32;    gamma [d_out] fp32 or NULL (unit scale);
+ *   residual, y  [B, d_out] bf16 (y may alias residual, not attn).
+ *   workspace    device, grok_decode_out_workspace_bytes(B, d_in, d_out)
+ *                bytes, 16-byte aligned, ZEROED before its first use: it
+ *                holds an arrival counter that every call leaves at zero.
+ *                Calls that overlap in time must not share a workspace.
+ * Errors: EINVAL for NULL pointers, B < 1, d_in or d_out not a positive
+ * multiple of 8, a bad eps, misaligned pointers (16 bytes; so and gamma 4),
+ * or overlaps with the workspace or of y with attn; ENOMEM if ws_bytes is too
+ * small.
+ */
+GROK_API size_t grok_decode_out_workspace_bytes(int B, int d_in, int d_out);
+GROK_API int grok_decode_out(const void *attn, const int8_t *wo_packed, const float *so,
+                             const float *gamma, float eps, const void *residual, void *y,
+                             void *workspace, size_t ws_bytes, int B, int d_in, int d_out,
+                             hipStream_t stream);
+
+/*
  * Rotary embedding, in place ([ch4] §4.3, §4.3.1): for x [B, T, H, D] and the
  * position p = offset[b] + t,
  *   inv_freq[i] = base^(-2i/D) (fp32),  theta_i = fp32(p * inv_freq[i]),

@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 24, syms
+    assert len(syms) == 26, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -230,6 +230,26 @@ def test_decode_qkv_validation(lib):
     assert "at most 2 rows" in _err(lib)
     assert call(prenorm=1, B=1, eps=-1.0) == EINVAL
     assert call(q=FAKE) == EINVAL and "overlaps x" in _err(lib)
+
+
+def test_decode_out_validation_and_workspace(lib):
+    wsb = lambda B, di, do: _c(lib, "grok_decode_out_workspace_bytes", i(B), i(di), i(do), restype=ctypes.c_size_t)
+    # counter (256 B), 384 workgroups x 4 row sums rounded up to 256 B, the bf16 projection
+    assert wsb(1, 6144, 6144) == 256 + 6144 + 6144 * 2
+    assert wsb(0, 6144, 6144) == 0 and wsb(1, 6140, 6144) == 0
+
+    def call(B=1, di=6144, do=6144, eps=1e-5, attn=FAKE, y=ctypes.c_void_p(0x400000), ws=ctypes.c_void_p(0x800000),
+             nbytes=1 << 20, so=FAKE):
+        return _c(lib, "grok_decode_out", attn, FAKE, so, None, fl(eps), FAKE, y, ws, ctypes.c_size_t(nbytes), i(B),
+                  i(di), i(do), None)
+    assert call(do=6140) == EINVAL
+    assert call(B=0) == EINVAL
+    assert call(eps=-1.0) == EINVAL
+    assert call(attn=None) == EINVAL
+    assert call(so=ctypes.c_void_p(0x10002)) == EINVAL            # 4-byte alignment
+    assert call(nbytes=100) == ENOMEM
+    assert call(y=FAKE) == EINVAL and "overlap" in _err(lib)     # y over attn
+    assert call(ws=ctypes.c_void_p(0x400000)) == EINVAL            # workspace over y
 
 
 def test_decode_append_validation(lib):

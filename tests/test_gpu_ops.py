@@ -651,6 +651,69 @@ def test_decode_sublayer(G, B, d, Hq, Hkv, lens, Tmax, fused):
     U.assert_bf16_close(y, ref, "decode sub-layer", magnitude=np.maximum(np.abs(ref), np.abs(nt)))
 
 
+@pytest.mark.parametrize("B,d_in,d_out,use_gamma", [
+    (1, 6144, 6144, False),   # one token at Grok-1's width: 384 workgroups meet through memory
+    (3, 1024, 1000, True),    # a partial last 16-channel block, gamma
+    (4, 8192, 512, True),     # the most rows of the widest input the fused form holds on chip
+    (5, 256, 264, False),     # more rows: projection and norm as two launches
+    (32, 1024, 2048, True),
+])
+def test_decode_out(G, B, d_in, d_out, use_gamma):
+    """Output projection + post-norm + residual (one launch up to 4 rows)
+    against the oracle's composition ([ch6] §6.3.1), against the separate
+    projection + norm calls (at most one bf16 rounding apart), and bit-stable
+    over repeated eager calls and graph replays (the arrival counter is
+    reset by each call)."""
+    grok, U, torch = G
+    g = gi.rng(9000 + B * 7 + d_out)
+    attn = gi.normal_bf16(g, (B, d_in))
+    x = gi.normal_bf16(g, (B, d_out))
+    w = gi.int8_uniform(g, (d_in, d_out))
+    so = (0.02 / 127 * g.uniform(0.5, 1.5, d_out)).astype(np.float32)
+    gm = g.uniform(0.5, 1.5, d_out).astype(np.float32) if use_gamma else None
+    da, dx = U.dev_bf16(attn), U.dev_bf16(x)
+    wp = grok.grok_linear_int8_pack(U.dev(w))
+    dso = U.dev(so)
+    dg = U.dev(gm) if use_gamma else None
+    ws = torch.zeros(grok.grok_decode_out_workspace_bytes(B, d_in, d_out), dtype=torch.uint8, device="cuda")
+    y = torch.empty((B, d_out), dtype=torch.bfloat16, device="cuda")
+    grok.grok_decode_out(da, wp, dso, dx, y, ws, gamma=dg, eps=1e-5)
+    torch.cuda.synchronize()
+    y0 = U.bits(y).copy()
+    a64, x64 = orc.bf16_bits_to_f64(attn), orc.bf16_bits_to_f64(x)
+    o = orc.linear_int8(a64, w, so, out="bf16")
+    ref = orc.rmsnorm(o, gm, 1e-5, residual=x64)
+    nt = ref - x64
+    U.assert_bf16_close(orc.bf16_bits_to_f64(y0), ref, f"decode_out B={B}", magnitude=np.maximum(np.abs(ref), np.abs(nt)))
+    # the separate calls: the same o, the norm's sum in another order
+    o_d = torch.empty((B, d_out), dtype=torch.bfloat16, device="cuda")
+    y_u = torch.empty_like(y)
+    grok.grok_linear_int8_gemv(da, [wp], [dso], [o_d])
+    grok.grok_rmsnorm(o_d, y_u, gamma=dg, residual=dx, eps=1e-5)
+    torch.cuda.synchronize()
+    yu = orc.bf16_bits_to_f64(U.bits(y_u))
+    yf = orc.bf16_bits_to_f64(y0)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(yu), 1e-30))[1] - 8)
+    assert np.all(np.abs(yf - yu) <= ulp), "fused and separate calls differ by more than one bf16 rounding"
+    assert np.mean(yf != yu) < 0.02
+    # repeated calls, eager and from a graph, give the same bits
+    for _ in range(2):
+        grok.grok_decode_out(da, wp, dso, dx, y, ws, gamma=dg, eps=1e-5)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(U.bits(y), y0)
+    gr = torch.cuda.CUDAGraph()
+    y.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        grok.grok_decode_out(da, wp, dso, dx, y, ws, gamma=dg, eps=1e-5)
+    for _ in range(3):
+        y.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(U.bits(y), y0)
+    assert int(ws[:4].view(torch.int32).item()) == 0  # the counter is back at zero
+
+
 # --------------------------------------------------------------------------
 # MoE FFN sub-layer
 # --------------------------------------------------------------------------
