@@ -23,7 +23,8 @@ __all__ = [
     "grok_rmsnorm", "grok_linear_int8", "grok_linear_int8_packed_bytes",
     "grok_linear_int8_pack", "grok_linear_int8_gemv", "grok_decode_qkv", "grok_decode_out",
     "grok_decode_out_workspace_bytes", "grok_rope", "grok_kv_append",
-    "grok_attn_prefill", "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
+    "grok_attn_prefill", "grok_attn_prefill_rope", "grok_attn_prefill_rope_workspace_bytes",
+    "grok_attn_prefill_chunk", "grok_attn_decode", "grok_attn_decode_append",
     "grok_attn_decode_append_noalloc", "grok_attn_decode_append_noalloc_max_bytes",
     "grok_attn_decode_workspace_bytes", "grok_moe_workspace_bytes", "grok_moe_interleave",
     "grok_moe_route", "grok_moe_ffn", "grok_prefill_qkv_workspace_bytes", "grok_prefill_qkv",
@@ -57,6 +58,8 @@ _PROTOS = {
     "grok_rope": (_i, [_p, _i, _i, _i, _i, _p, _f, _i, _p]),
     "grok_kv_append": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
     "grok_attn_prefill": (_i, [_p, _p, _p, _i64, _p, _p, _i, _i, _i, _i, _i, _f, _f, _i, _p]),
+    "grok_attn_prefill_rope_workspace_bytes": (_sz, [_i, _i]),
+    "grok_attn_prefill_rope": (_i, [_p, _p, _p, _i64, _p, _p, _p, _sz, _i, _i, _i, _i, _i, _f, _f, _f, _p]),
     "grok_attn_decode": (_i, [_p, _p, _p, _p, _p, _p, _sz, _p, _i, _i, _i, _i, _i, _f, _f, _p]),
     "grok_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "grok_attn_prefill_chunk": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _f, _p]),
@@ -299,6 +302,28 @@ def grok_attn_prefill(q, k, v, out, attn_mult, softcap=30.0, key_valid=None):
     _check(lib.grok_attn_prefill(_ptr(q), _ptr(k), _ptr(v), kv_rows, _ptr(key_valid), _ptr(out),
                                  B, T, Hq, Hkv, D, attn_mult, softcap, _dtype_code(q), _stream(q)),
            "grok_attn_prefill")
+    return out
+
+
+def grok_attn_prefill_rope_workspace_bytes(T, D=128) -> int:
+    return int(lib.grok_attn_prefill_rope_workspace_bytes(T, D))
+
+
+def grok_attn_prefill_rope(q, k, v, out, workspace, attn_mult, softcap=30.0, key_valid=None, rope_base=10000.0):
+    """Causal GQA with q rotated at positions 0..T-1 inside the kernel (q is not
+    modified; k must be rotated already); bf16, D = 128."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(out, "out", torch.bfloat16)
+    _need(workspace, "workspace")
+    _need(key_valid, "key_valid", torch.uint8, 2)
+    B, T, Hq, D = q.shape
+    kv_rows, Hkv = k.shape[1], k.shape[2]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.grok_attn_prefill_rope(_ptr(q), _ptr(k), _ptr(v), kv_rows, _ptr(key_valid), _ptr(out),
+                                      _ptr(workspace), ws_bytes, B, T, Hq, Hkv, D, attn_mult, softcap, rope_base,
+                                      _stream(q)), "grok_attn_prefill_rope")
     return out
 
 

@@ -97,5 +97,22 @@ __device__ __forceinline__ void lds_wait(u32x2 *lo, u32x2 *hi) {
                : "i"(kLeft));
 }
 
+// RoPE of 8 bf16 pairs held by one lane: element e of w1 is dim i0 + e, element
+// e of w2 dim i0 + e + 64 (the half-split partner), with the cos/sin of those
+// pairs; rope_rotate of common.h, rounded to bf16 as grok_rope rounds.
+__device__ __forceinline__ void rope8(u32x4 &w1, u32x4 &w2, const float *cs, const float *sn) {
+  u32x4 o1, o2;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a0, a1, b0, b1;
+    rope_rotate(lo_bf16(w1[q]), lo_bf16(w2[q]), cs[2 * q], sn[2 * q], a0, b0);
+    rope_rotate(hi_bf16(w1[q]), hi_bf16(w2[q]), cs[2 * q + 1], sn[2 * q + 1], a1, b1);
+    o1[q] = pack_bf16x2(a0, a1);
+    o2[q] = pack_bf16x2(b0, b1);
+  }
+  w1 = o1;
+  w2 = o2;
+}
+
 }  // namespace attn
 }  // namespace grok

@@ -148,7 +148,11 @@ hipError_t launch_prefill_generic(const void *q, const void *k, const void *v, i
 hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int64_t kv_rows,
                                const uint8_t *key_valid, void *out, int B, int T, int Hq,
                                int Hkv, float mult, float cap, hipStream_t s,
-                               const int32_t *offset = nullptr, int32_t *status = nullptr);
+                               const int32_t *offset = nullptr, int32_t *status = nullptr,
+                               const float *rtab = nullptr);
+// cos/sin of rope_phase for positions 0..npos-1 and the D/2 = 64 pairs:
+// tab[p][i] = cos, tab[p][64 + i] = sin (linear_int8.hip).
+hipError_t launch_rope_table(float *tab, int npos, const RopeFreqs &f, hipStream_t s);
 bool prefill_mfma_supported(int64_t kv_rows, int Hq, int Hkv, int D, int dtype);
 hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int32_t *kv_len,
                          void *out, void *ws, int32_t *status, int B, int Tmax, int Hq, int Hkv,

@@ -75,22 +75,6 @@ struct DecodeArgs {
   float inv[kD / 2];      // RoPE inv_freq
 };
 
-// Rotate the 8 bf16 pairs (x1 in w1, x2 in w2, element e <-> dim i0 + e and
-// i0 + e + 64) with the cos/sin table, rounding to bf16.
-__device__ __forceinline__ void rope8(u32x4 &w1, u32x4 &w2, const float *cs, const float *sn) {
-  u32x4 o1, o2;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float a0, a1, b0, b1;
-    rope_rotate(lo_bf16(w1[q]), lo_bf16(w2[q]), cs[2 * q], sn[2 * q], a0, b0);
-    rope_rotate(hi_bf16(w1[q]), hi_bf16(w2[q]), cs[2 * q + 1], sn[2 * q + 1], a1, b1);
-    o1[q] = pack_bf16x2(a0, a1);
-    o2[q] = pack_bf16x2(b0, b1);
-  }
-  w1 = o1;
-  w2 = o2;
-}
-
 template <bool kAppend>
 __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[kSplit * kRowBytes];

@@ -257,6 +257,41 @@ int grok_attn_prefill(const void *q, const void *k, const void *v, int64_t kv_ro
                     "attn_prefill");
 }
 
+size_t grok_attn_prefill_rope_workspace_bytes(int T, int D) {
+  if (T < 1 || D != 128) return 0;
+  return static_cast<size_t>(T) * 128 * sizeof(float);
+}
+
+int grok_attn_prefill_rope(const void *q, const void *k, const void *v, int64_t kv_rows, const uint8_t *key_valid,
+                           void *out, void *workspace, size_t ws_bytes, int B, int T, int Hq, int Hkv, int D,
+                           float attn_mult, float softcap, float rope_base, hipStream_t stream) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1) return fail(GROK_EINVAL, "attn_prefill_rope: bad shape");
+  if (Hq % Hkv) return fail(GROK_EINVAL, "attn_prefill_rope: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (D != 128) return fail(GROK_EINVAL, "attn_prefill_rope: head size must be 128 (D=%d)", D);
+  if (kv_rows < T) return fail(GROK_EINVAL, "attn_prefill_rope: kv_rows=%lld < T=%d", (long long)kv_rows, T);
+  if (bad_softmax_params(attn_mult, softcap))
+    return fail(GROK_EINVAL, "attn_prefill_rope: attn_mult must be finite and softcap in (0, 40]");
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return fail(GROK_EINVAL, "attn_prefill_rope: bad rope_base");
+  if (!q || !k || !v || !out || !workspace) return fail(GROK_EINVAL, "attn_prefill_rope: null pointer");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
+                       reinterpret_cast<uintptr_t>(workspace);
+  if (al % 16) return fail(GROK_EINVAL, "attn_prefill_rope: misaligned pointer");
+  const size_t need = static_cast<size_t>(T) * 128 * sizeof(float);
+  if (ws_bytes < need) return fail(GROK_ENOMEM, "attn_prefill_rope: workspace %zu bytes < %zu needed", ws_bytes, need);
+  const size_t nq = static_cast<size_t>(B) * T * Hq * D * 2;
+  if (overlaps(out, nq, q, nq) || overlaps(workspace, need, q, nq) || overlaps(workspace, need, out, nq))
+    return fail(GROK_EINVAL, "attn_prefill_rope: out or the workspace overlaps q, or the workspace overlaps out");
+  grok::RopeFreqs f;
+  grok::rope_build_freqs(D, rope_base, &f);
+  float *tab = static_cast<float *>(workspace);
+  hipError_t e = grok::launch_rope_table(tab, T, f, stream);
+  if (e != hipSuccess) return hip_status(e, "attn_prefill_rope: table");
+  return hip_status(grok::launch_prefill_mfma(q, k, v, kv_rows, key_valid, out, B, T, Hq, Hkv, attn_mult, softcap,
+                                              stream, nullptr, nullptr, tab),
+                    "attn_prefill_rope");
+}
+
 size_t grok_attn_decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv, int D) {
   if (B < 1 || Tmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D != 128) return 0;
   return grok::decode_workspace_bytes(B, Tmax, Hq, Hkv);

@@ -507,14 +507,18 @@ __global__ __launch_bounds__(64) void rope_table_kernel(float *tab, RopeFreqs f)
 
 size_t prefill_qkv_workspace_bytes(int Tmax) { return static_cast<size_t>(Tmax) * 128 * sizeof(float); }
 
+hipError_t launch_rope_table(float *tab, int npos, const RopeFreqs &f, hipStream_t s) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(npos), dim3(64), 0, s, tab, f);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_qkv(const void *x, const PrefillQkvArgs &qa_in, void *workspace, int d, float rope_base,
                               hipStream_t s) {
   RopeFreqs f;
   rope_build_freqs(kBN, rope_base, &f);
   PrefillQkvArgs qa = qa_in;
   qa.rtab = static_cast<const float *>(workspace);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(qa.Tmax), dim3(64), 0, s, static_cast<float *>(workspace), f);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_rope_table(static_cast<float *>(workspace), qa.Tmax, f, s);
   if (e != hipSuccess) return e;
   const int64_t M = static_cast<int64_t>(qa.B) * qa.T;
   const int64_t gm = (M + kBM - 1) / kBM;

@@ -65,13 +65,17 @@ struct PrefillArgs {
   int64_t kv_rows;
   int B, T, Hq, Hkv, G, Gc, npb, nhc, nqt;
   float k1, k2inv;  // exp2 scale inside the softcap; 1 / (outer exp2 scale)
+  const float *rtab;  // kRopeQ: [T][128] cos of pairs 0..63, then sin, per position
 };
 
 // kOffset: the T query rows of sequence b sit at positions offset[b] + t (a
 // chunk after a cached prefix) and attend keys [0, offset[b] + t] of K/V
 // read in place from the cache (kv_rows = its capacity); without it the
 // offset is 0 and the code is the plain causal prefill.
-template <bool kHasValid, bool kOffset>
+// kRopeQ: q arrives unrotated and each query row is rotated at its position
+// while its fragments are loaded (ch. 4 §4.3.1), from the table rtab of
+// rope_phase values: the bits of grok_rope followed by the plain prefill.
+template <bool kHasValid, bool kOffset, bool kRopeQ = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][kTileBytes];
@@ -221,11 +225,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     const int row = pos[i] - o;
     const bool ok = row < a.T;
     const bf16_t *qp = a.q + ((static_cast<int64_t>(b) * a.T + (ok ? row : 0)) * a.Hq + head[i]) * kD;
+    u32x4 w[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 w = ok ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * lg) : u32x4{0, 0, 0, 0};
-      qf[i][kk] = __builtin_bit_cast(bf16x8, w);
+    for (int kk = 0; kk < 4; ++kk) w[kk] = ok ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * lg) : u32x4{0, 0, 0, 0};
+    if constexpr (kRopeQ) {
+      // dims d (kk = 0, 1) pair with d + 64 (kk + 2) in the same lane
+      const float *tp = a.rtab + static_cast<int64_t>(ok ? row : 0) * kD + 8 * lg;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float cs[8], sn[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cs[e] = tp[32 * kk + e];
+          sn[e] = tp[64 + 32 * kk + e];
+        }
+        rope8(w[kk], w[kk + 2], cs, sn);
+      }
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[i][kk] = __builtin_bit_cast(bf16x8, w[kk]);
   }
 
   f32x4 oacc[kRB][8];
@@ -428,8 +446,9 @@ bool prefill_mfma_supported(int64_t kv_rows, int Hq, int Hkv, int D, int dtype) 
 hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int64_t kv_rows,
                                const uint8_t *key_valid, void *out, int B, int T, int Hq,
                                int Hkv, float mult, float cap, hipStream_t s,
-                               const int32_t *offset, int32_t *status) {
+                               const int32_t *offset, int32_t *status, const float *rtab) {
   PrefillArgs a;
+  a.rtab = rtab;
   a.offset = offset;
   a.status = status;
   a.q = static_cast<const bf16_t *>(q);
@@ -452,7 +471,14 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v, int6
   const int64_t nblk = static_cast<int64_t>(B) * Hkv * a.nhc * a.nqt;
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (offset && key_valid) return hipErrorInvalidValue;  // validated by the caller
-  if (offset)
+  if (rtab && offset) return hipErrorInvalidValue;
+  if (rtab && key_valid)
+    hipLaunchKernelGGL((prefill_mfma_kernel<true, false, true>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+                       s, a);
+  else if (rtab)
+    hipLaunchKernelGGL((prefill_mfma_kernel<false, false, true>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
+                       0, s, a);
+  else if (offset)
     hipLaunchKernelGGL((prefill_mfma_kernel<false, true>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
                        s, a);
   else if (key_valid)

@@ -8,7 +8,8 @@ owns device memory).
   "model.py close reading, part 1", §4.4): RoPE q and the new k at step[b],
   append k/v to the cache, attend slots [0, step[b]+1) -- one fused call.
 * ``PrefillStep``  -- a prompt with no cache (same page, §4.3.1 and §4.5):
-  RoPE q and k at positions 0..T-1, causal GQA attention.
+  RoPE q and k at positions 0..T-1, causal GQA attention (optionally with q
+  rotated inside the attention kernel).
 * ``SublayerStep`` -- the attention half of a decoder layer (ch. 6 "model.py
   close reading, part 3", §6.3.1): h = x + norm(Wo . attn(rope(Wq n),
   rope(Wk n), Wv n)) with n = norm(x).
@@ -29,7 +30,8 @@ from __future__ import annotations
 import torch
 
 from . import (grok_attn_decode, grok_attn_decode_append, grok_attn_decode_workspace_bytes,
-               grok_attn_prefill, grok_attn_prefill_chunk,
+               grok_attn_prefill, grok_attn_prefill_chunk, grok_attn_prefill_rope,
+               grok_attn_prefill_rope_workspace_bytes,
                grok_decode_out, grok_decode_out_workspace_bytes, grok_decode_qkv, grok_kv_append, grok_linear_int8, grok_linear_int8_gemv,
                grok_linear_int8_pack, grok_moe_ffn, grok_moe_interleave, grok_moe_workspace_bytes,
                grok_prefill_qkv, grok_prefill_qkv_workspace_bytes, grok_rmsnorm, grok_rope)
@@ -89,18 +91,30 @@ class DecodeStep:
 
 
 class PrefillStep:
-    def __init__(self, q, k, v, attn_mult, softcap=30.0, rope_base=10000.0, key_valid=None):
+    """A prompt with no cache: RoPE of q and k at positions 0..T-1, then the
+    causal attention. fused_rope (bf16, D = 128): k is rotated in place by its
+    own pass and q inside the attention kernel (q is left unrotated);
+    otherwise (the default) both are rotated in place first."""
+
+    def __init__(self, q, k, v, attn_mult, softcap=30.0, rope_base=10000.0, key_valid=None, fused_rope=False):
         self.q, self.k, self.v = q, k, v
         self.attn_mult, self.softcap, self.rope_base = attn_mult, softcap, rope_base
         self.key_valid = key_valid
         B, T, Hq, D = q.shape
+        self.fused_rope = fused_rope
         self.out = torch.empty((B, T, Hq * D), dtype=q.dtype, device=q.device)
+        self.ws = (torch.empty(grok_attn_prefill_rope_workspace_bytes(T, D), dtype=torch.uint8, device=q.device)
+                   if fused_rope else None)
 
     def rope(self):
-        grok_rope(self.q, None, self.rope_base)
+        if not self.fused_rope:
+            grok_rope(self.q, None, self.rope_base)
         grok_rope(self.k, None, self.rope_base)
 
     def attend(self):
+        if self.fused_rope:
+            return grok_attn_prefill_rope(self.q, self.k, self.v, self.out, self.ws, self.attn_mult, self.softcap,
+                                          key_valid=self.key_valid, rope_base=self.rope_base)
         return grok_attn_prefill(self.q, self.k, self.v, self.out, self.attn_mult, self.softcap,
                                  key_valid=self.key_valid)
 

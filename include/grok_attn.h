@@ -282,6 +282,28 @@ GROK_API int grok_attn_prefill_chunk(const void *q, const void *k_cache, const v
                                      float softcap, hipStream_t stream);
 
 /*
+ * grok_attn_prefill with the rotation of q folded in ([ch4] §4.3.1 RoPE,
+ * §4.5.2-§4.5.4 attention): q arrives unrotated and every query row t is
+ * rotated at position t while it is loaded, with the numerics (and the bits)
+ * of grok_rope(q) followed by grok_attn_prefill; q itself is not modified.
+ * k must already be rotated (grok_rope, or the cache written by
+ * grok_kv_append / grok_prefill_qkv); mask, layout and the fully-masked-row
+ * rule as for grok_attn_prefill. bf16 and D = 128 only.
+ *   workspace  device, grok_attn_prefill_rope_workspace_bytes(T, 128) bytes
+ *              (the cos/sin table of positions 0..T-1, rebuilt by each call;
+ *              one launch before the attention kernel).
+ * Errors: EINVAL as for grok_attn_prefill, D != 128, a bad rope_base, or out
+ * or the workspace overlapping q (or each other); ENOMEM if ws_bytes is too
+ * small.
+ */
+GROK_API size_t grok_attn_prefill_rope_workspace_bytes(int T, int D);
+GROK_API int grok_attn_prefill_rope(const void *q, const void *k, const void *v, int64_t kv_rows,
+                                    const uint8_t *key_valid, void *out, void *workspace,
+                                    size_t ws_bytes, int B, int T, int Hq, int Hkv, int D,
+                                    float attn_mult, float softcap, float rope_base,
+                                    hipStream_t stream);
+
+/*
  * Single-token decode attention against a KV cache ([ch4] §4.4, §4.5; the
  * causal mask of one query is all-ones and the memory mask keeps slots
  * j < kv_len[b]):

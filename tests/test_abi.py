@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = declared_symbols()
-    assert len(syms) == 26, syms
+    assert len(syms) == 28, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -139,6 +139,24 @@ def test_prefill_validation(lib):
     assert call(dtype=3) == EINVAL
     assert call(q=None) == EINVAL
     assert call(D=128, dtype=0, q=ctypes.c_void_p(0x10004)) == EINVAL  # MFMA path needs 16-B alignment
+
+
+def test_prefill_rope_validation(lib):
+    wsb = lambda T, D: _c(lib, "grok_attn_prefill_rope_workspace_bytes", i(T), i(D), restype=ctypes.c_size_t)
+    assert wsb(8192, 128) == 8192 * 512 and wsb(8192, 64) == 0 and wsb(0, 128) == 0
+
+    def call(B=1, T=100, Hq=48, Hkv=8, D=128, base=1e4, cap=30.0, q=FAKE, out=ctypes.c_void_p(0x4000000),
+             ws=ctypes.c_void_p(0x8000000), nbytes=1 << 20):
+        return _c(lib, "grok_attn_prefill_rope", q, FAKE, FAKE, i64(T), None, out, ws, ctypes.c_size_t(nbytes), i(B),
+                  i(T), i(Hq), i(Hkv), i(D), fl(0.088), fl(cap), fl(base), None)
+    assert call(D=64) == EINVAL
+    assert call(Hq=44) == EINVAL
+    assert call(base=0.0) == EINVAL
+    assert call(cap=50.0) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(nbytes=100) == ENOMEM
+    assert call(out=FAKE) == EINVAL and "overlaps" in _err(lib)   # out over q
+    assert call(ws=FAKE) == EINVAL                                  # table over q
 
 
 def test_decode_validation_and_workspace(lib):

@@ -47,6 +47,8 @@ def test_prefill_step_graph_replays_match_eager(G):
     q, k = q0.clone(), k0.clone()
     st = pipe.PrefillStep(q, k, U.dev_bf16(p["v"]), 4 / math.sqrt(128))
     eager = U.bits(st())
+    fused = pipe.PrefillStep(q0.clone(), k0.clone(), U.dev_bf16(p["v"]), 4 / math.sqrt(128), fused_rope=True)
+    np.testing.assert_array_equal(U.bits(fused()), eager)  # q rotated in the kernel: the same bits
     graph = pipe.capture(st)
     for rep in range(3):
         q.copy_(q0)

@@ -375,6 +375,40 @@ def test_prefill_chunk_at_offset_zero_is_the_prefill_bit_for_bit_and_bad_offsets
     assert not np.any(U.host(a))
 
 
+@pytest.mark.parametrize("B,T,Hq,Hkv,padded", [
+    (1, 200, 48, 8, False),   # Grok-1 heads, a ragged last query tile
+    (2, 129, 8, 8, False),    # MHA, two sequences
+    (1, 64, 6, 1, False),     # MQA, one tile
+    (2, 150, 12, 2, True),    # key padding (and a fully masked row in sequence 1)
+])
+def test_prefill_rope_matches_rope_then_prefill(G, B, T, Hq, Hkv, padded):
+    """q rotated inside the attention kernel gives the bits of grok_rope(q)
+    followed by grok_attn_prefill, and leaves q as it was."""
+    grok, U, torch = G
+    p = gi.make_prefill_inputs(B, T, Hq, Hkv, 128, seed=31 * T + Hq)
+    q, k, v = U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"])
+    grok.grok_rope(k, None, 1e4)
+    kv = None
+    if padded:
+        g = gi.rng(7 + T)
+        m = (g.uniform(size=(B, T)) > 0.3).astype(np.uint8)
+        m[1, :] = 0
+        m[1, T // 2:] = 1  # rows below T/2 of sequence 1 see no valid key
+        kv = U.dev(m)
+    mult = 1 / math.sqrt(128)
+    ws = torch.empty(grok.grok_attn_prefill_rope_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    out_f = torch.empty((B, T, Hq * 128), dtype=torch.bfloat16, device="cuda")
+    grok.grok_attn_prefill_rope(q, k, v, out_f, ws, mult, 30.0, key_valid=kv)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(U.bits(q), p["q"])  # q untouched
+    q2 = q.clone()
+    grok.grok_rope(q2, None, 1e4)
+    out_u = torch.empty_like(out_f)
+    grok.grok_attn_prefill(q2, k, v, out_u, mult, 30.0, key_valid=kv)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(U.bits(out_f), U.bits(out_u))
+
+
 def test_prefill_mfma_padding_and_fully_masked_rows(G):
     B, T = 2, 77
     pad = np.ones((B, T), np.uint8)
