@@ -347,7 +347,7 @@ def _cpu_model():
 
 def cpu_baseline():
     """The fp64 oracle (NumPy, one thread per worker process) on the host cores:
-    a bounded sample of the 8k prefill (all 48 heads of 12 query rows per
+    a bounded sample of the 8k prefill (all 48 heads of 96 query rows per
     worker, spread over the sequence), and the tiny fp32 prefill, the
     one-sequence decode and the 32-sequence ragged decode in full."""
     import gqa_inputs as gi
@@ -356,7 +356,7 @@ def cpu_baseline():
     w = gi.WORKLOADS["prefill_b1_t8192"]
     p = gi.make_workload(w.name)
     T = w.T
-    rows = np.linspace(0, T - 1, 12 * workers).astype(np.int64)
+    rows = np.linspace(0, T - 1, 96 * workers).astype(np.int64)
     # one task per worker, rows interleaved so that each holds short and long rows
     tasks = [(rows[i::workers], p["q"][:, rows[i::workers]]) for i in range(workers)]
     sec = _timed_pool(w.name, _oracle_prefill_rows, tasks, workers, (p["k"], p["v"]))
