@@ -56,6 +56,7 @@ constexpr int kD = 128;
 constexpr int kSplit = 128;  // cache slots per workgroup
 constexpr int kSplitWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kXcds = 8;  // dies of the device: workgroup i is dispatched to die i % 8
 
 struct DecodeArgs {
   const bf16_t *q, *kc, *vc;
@@ -81,7 +82,25 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   __shared__ float red_l[kSplitWaves][16];
   __shared__ __attribute__((aligned(16))) float rcs[kAppend ? kD / 2 : 1], rsn[kAppend ? kD / 2 : 1];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Workgroup -> (split s, KV head g, sequence b). Die x = blockIdx.x % 8
+  // takes, sequence by sequence with splits fastest, the KV heads g with
+  // (b + g) % 8 == x: each die gets one head of every sequence (the same work
+  // per die for any length mix) and the head it reads rotates with b. With a
+  // KV head count that is not a multiple of 8, die x takes the pairs
+  // b * Hkv + g = x (mod 8).
+  const int xi = blockIdx.x % kXcds, xj = blockIdx.x / kXcds;
+  const int pl = xj / a.S, s = xj % a.S;
+  int b, g;
+  if (a.Hkv % kXcds == 0) {
+    const int hk = a.Hkv / kXcds;
+    b = pl / hk;
+    g = (xi - b % kXcds + kXcds) % kXcds + kXcds * (pl % hk);
+  } else {
+    const int pair = xi + kXcds * pl;
+    b = pair / a.Hkv;
+    g = pair % a.Hkv;
+  }
+  if (b >= a.B) return;
   const int len = kAppend ? a.step[b] + 1 : a.kv_len[b];
   if (kAppend && s == 0 && g == 0 && threadIdx.x == 0 && a.new_step)
     a.new_step[b] = (len >= 1 && len <= a.Tmax) ? len : len - 1;
@@ -366,6 +385,16 @@ hipError_t decode_static_scratch(void **ptr) {
   return hipSuccess;
 }
 
+namespace {
+// One workgroup per (split, pair) slot, the pairs rounded up to a multiple of
+// the die count; 0 when that does not fit a grid dimension.
+int64_t split_blocks(const DecodeArgs &a) {
+  const int64_t pairs = static_cast<int64_t>(a.B) * a.Hkv;
+  const int64_t n = kXcds * ((pairs + kXcds - 1) / kXcds) * a.S;
+  return n > 0x7fffffff ? 0 : n;
+}
+}  // namespace
+
 size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv) {
   const size_t S = (static_cast<size_t>(Tmax) + kSplit - 1) / kSplit;
   const size_t G = static_cast<size_t>(Hq / Hkv);
@@ -400,7 +429,10 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
   a.step = nullptr;
   a.new_step = nullptr;
   a.q_out = nullptr;
-  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.S, Hkv, B), dim3(kSplitWaves * kWave), 0, st, a);
+  const int64_t nblk = split_blocks(a);
+  if (nblk == 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(kSplitWaves * kWave), 0, st,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);
@@ -438,7 +470,10 @@ hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, v
   a.new_step = new_step;
   a.q_out = static_cast<bf16_t *>(q_out);
   for (int i = 0; i < kD / 2; ++i) a.inv[i] = f.inv[i];
-  hipLaunchKernelGGL(decode_split_kernel<true>, dim3(a.S, Hkv, B), dim3(kSplitWaves * kWave), 0, st, a);
+  const int64_t nblk = split_blocks(a);
+  if (nblk == 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(decode_split_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(kSplitWaves * kWave), 0, st,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);

@@ -922,7 +922,7 @@ def test_slot_insertion_into_a_batched_cache_then_batched_decode(G):
     qn, kn, vn = (gi.normal_bf16(g, (B, 1, Hq, D)), gi.normal_bf16(g, (B, 1, Hkv, D)),
                   gi.normal_bf16(g, (B, 1, Hkv, D)))
     dout = torch.empty((B, 1, Hq * D), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
     kc_before, vc_before = orc.bf16_bits_to_f64(U.bits(kc)), orc.bf16_bits_to_f64(U.bits(vc))
     grok.grok_attn_decode_append(U.dev_bf16(qn), U.dev_bf16(kn), U.dev_bf16(vn), kc, vc, U.dev(step), dout, ws,
                                  mult, status=status)

@@ -29,7 +29,7 @@ def _compare(grok, torch, dev_bf16, dev, p, attn_mult, softcap=30.0):
             grok.grok_attn_decode_append_noalloc(q, kn, vn, kc, vc, step, out, attn_mult, softcap,
                                                  new_step=new_step, q_out=q_out, status=status)
         else:
-            ws = torch.empty(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8,
+            ws = torch.zeros(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8,
                              device="cuda")
             grok.grok_attn_decode_append(q, kn, vn, kc, vc, step, out, ws, attn_mult, softcap,
                                          new_step=new_step, q_out=q_out, status=status)
