@@ -66,6 +66,7 @@ struct DecodeArgs {
   float *part_l;  // [B, Hkv, S, G]
   int32_t *status;
   int B, Tmax, Hq, Hkv, G, S, split_keys;
+  int by_die;  // workgroup layout: by die (several sequences) or splits fastest
   float k1, k2inv;
   // fused append: q is unrotated, len = step[b] + 1
   const bf16_t *kn, *vn;  // [B, Hkv, D] new k (unrotated), v
@@ -87,11 +88,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   // (b + g) % 8 == x: each die gets one head of every sequence (the same work
   // per die for any length mix) and the head it reads rotates with b. With a
   // KV head count that is not a multiple of 8, die x takes the pairs
-  // b * Hkv + g = x (mod 8).
+  // b * Hkv + g = x (mod 8). A single sequence runs with splits fastest, heads
+  // next (measured faster for it).
   const int xi = blockIdx.x % kXcds, xj = blockIdx.x / kXcds;
-  const int pl = xj / a.S, s = xj % a.S;
-  int b, g;
-  if (a.Hkv % kXcds == 0) {
+  const int pl = xj / a.S;
+  int s = xj % a.S, b, g;
+  if (!a.by_die) {
+    s = blockIdx.x % a.S;
+    g = (blockIdx.x / a.S) % a.Hkv;
+    b = blockIdx.x / (a.S * a.Hkv);
+  } else if (a.Hkv % kXcds == 0) {
     const int hk = a.Hkv / kXcds;
     b = pl / hk;
     g = (xi - b % kXcds + kXcds) % kXcds + kXcds * (pl % hk);
@@ -418,6 +424,7 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
   a.G = Hq / Hkv;
   a.split_keys = kSplit;
   a.S = (Tmax + kSplit - 1) / kSplit;
+  a.by_die = B > 1;
   const size_t n = static_cast<size_t>(B) * Hkv * a.S * a.G;
   a.part_o = static_cast<float *>(ws);
   a.part_l = a.part_o + n * kD;
@@ -456,6 +463,7 @@ hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, v
   a.G = Hq / Hkv;
   a.split_keys = kSplit;
   a.S = (Tmax + kSplit - 1) / kSplit;
+  a.by_die = B > 1;
   const size_t n = static_cast<size_t>(B) * Hkv * a.S * a.G;
   a.part_o = static_cast<float *>(ws);
   a.part_l = a.part_o + n * kD;
