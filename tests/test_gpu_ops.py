@@ -459,6 +459,7 @@ def test_prefill_generic(G, B, T, Hq, Hkv, D, dtype, padded):
     (16, 1, [33, 300], 512),
     (8, 8, [5, 256], 256),
     (6, 3, [200, 77, 1], 200),  # capacity not a multiple of the 128-slot split
+    (32, 16, [3, 500, 129], 640),  # two KV heads per die and sequence in the split layout
 ])
 def test_decode(G, Hq, Hkv, lens, Tmax):
     grok, U, torch = G
