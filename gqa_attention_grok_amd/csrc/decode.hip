@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   // per die for any length mix) and the head it reads rotates with b. With a
   // KV head count that is not a multiple of 8, die x takes the pairs
   // b * Hkv + g = x (mod 8). A single sequence runs with splits fastest, heads
-  // next (measured faster for it).
+  // next (measured faster for it). Only speed depends on the dispatch order:
+  // every (split, KV head, sequence) has exactly one workgroup either way.
   const int xi = blockIdx.x % kXcds, xj = blockIdx.x / kXcds;
   const int pl = xj / a.S;
   int s = xj % a.S, b, g;
