@@ -460,6 +460,8 @@ def test_prefill_generic(G, B, T, Hq, Hkv, D, dtype, padded):
     (8, 8, [5, 256], 256),
     (6, 3, [200, 77, 1], 200),  # capacity not a multiple of the 128-slot split
     (32, 16, [3, 500, 129], 640),  # two KV heads per die and sequence in the split layout
+    (48, 8, [1, 900, 300, 1024, 129, 2, 640, 511, 777, 128, 1000], 1024),  # 11 sequences over 8 dies
+    (8, 2, [100, 1, 513, 257, 64, 384, 200], 600),  # 14 (sequence, KV head) pairs: 2 empty die slots
 ])
 def test_decode(G, Hq, Hkv, lens, Tmax):
     grok, U, torch = G
