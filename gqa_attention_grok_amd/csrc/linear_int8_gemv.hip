@@ -101,7 +101,10 @@ __device__ __forceinline__ void tie_after_wait(u32x4 *w, u32x4 *x) {
 // when a step is consumed, the (D-1) * kLoads loads of the later steps may
 // still be in flight (loads return in issue order; the compiler's own waits
 // get this count wrong at the loop head). Steps past the range re-read its
-// last tile (a cache hit) and are not consumed.
+// last tile (a cache hit) and are not consumed. A wave with no tiles (fewer
+// tiles than waves) issues and waits for its loads all the same, on tile 0:
+// no load or wait depends on a branch, so the compiler cannot give the
+// registers of a load still in flight to another value on some path.
 template <int MT, int NB, int D, bool XL>
 struct TileRing {
   static constexpr int kLoads = XL ? NB : NB + 2 * MT;  // load instructions per step
@@ -112,10 +115,9 @@ struct TileRing {
   const bf16_t *xr[MT];  // this lane's x rows (clamped into x; zeroed past M when used)
   int i0, i1, K, M, g, i16;
 
-  __device__ __forceinline__ bool busy() const { return i1 > i0; }
-
   __device__ __forceinline__ void issue(int slot, int i) {
-    const int ic = i < i1 ? i : i1 - 1;
+    const int il = i < i1 ? i : i1 - 1;
+    const int ic = il > 0 ? il : 0;
 #pragma unroll
     for (int v = 0; v < NB; ++v) wr[slot][v] = load16(wb[v] + static_cast<int64_t>(ic) * kTileBytes);
     if constexpr (!XL) {
@@ -130,10 +132,8 @@ struct TileRing {
   }
 
   __device__ __forceinline__ void prologue() {
-    if (busy()) {
 #pragma unroll
-      for (int u = 0; u < D; ++u) issue(u, i0 + u);
-    }
+    for (int u = 0; u < D; ++u) issue(u, i0 + u);
   }
 
   __device__ __forceinline__ void run(const bf16_t *xs, f32x4 (&acc)[NB][MT]) {
@@ -141,7 +141,6 @@ struct TileRing {
     for (int v = 0; v < NB; ++v)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[v][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!busy()) return;
     for (int c0 = i0; c0 < i1; c0 += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
@@ -212,15 +211,11 @@ struct XStage {
       st[r] = load16(x + 8 * static_cast<int64_t>(c < n8 ? c : 0));
     }
   }
-  // `left` ring loads issued after these may stay in flight.
-  template <int kLeftBusy, bool kNorm>
-  __device__ __forceinline__ void store(bf16_t *xs, bool busy, int M, int K, const float *gamma,
-                                        float eps, float *red /* [kWaves][4] */) {
-    if (busy) {
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLeftBusy) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+  // The kLeft ring loads issued after these may stay in flight.
+  template <int kLeft, bool kNorm>
+  __device__ __forceinline__ void store(bf16_t *xs, int M, int K, const float *gamma, float eps,
+                                        float *red /* [kWaves][4] */) {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLeft) : "memory");
 #pragma unroll
     for (int r = 0; r < kStage; ++r) asm volatile("" : "+v"(st[r]));  // uses stay below the wait
     const int n8 = M * K / 8;
@@ -316,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
   extern __shared__ f32x4 xs4[];  // XL: x rows [M][K] bf16
   __shared__ float red[kWaves][XL ? 4 : kMaxRows][NB * kTileCols];
   const int tid = threadIdx.x;
-  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave, g = l / 16, i16 = l % 16;
   const int M = a.M, K = a.K, KP = a.KP;
   const MatSel ms(a, blockIdx.x);
   const int j0 = ms.lw * NB;
@@ -340,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void gemv_packed_kernel(GemvArgs a) {
   ring.prologue();
   bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
   if constexpr (XL)
-    xst.template store<D * TileRing<MT, NB, D, XL>::kLoads, false>(xs, ring.busy(), M, K, nullptr, 0.f,
+    xst.template store<D * TileRing<MT, NB, D, XL>::kLoads, false>(xs, M, K, nullptr, 0.f,
                                                                     &red[0][0][0]);
   f32x4 acc[NB][MT];
   ring.run(xs, acc);
@@ -401,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void decode_qkv_kernel(QkvArgs qa) {
   __shared__ float red[kWaves][XL ? 4 : kMaxRows][NB * kTileCols];
   const GemvArgs &a = qa.g;
   const int tid = threadIdx.x;
-  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave, g = l / 16, i16 = l % 16;
   const int M = a.M, K = a.K, KP = a.KP;
   const MatSel ms(a, blockIdx.x);
   // blocks (jA, jA + 4) with jA % 8 < 4: channels c and c + 64 of one head
@@ -424,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void decode_qkv_kernel(QkvArgs qa) {
   ring.prologue();
   bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
   if constexpr (XL)
-    xst.template store<D * TileRing<MT, NB, D, XL>::kLoads, kNorm>(xs, ring.busy(), M, K, qa.gamma, qa.eps,
+    xst.template store<D * TileRing<MT, NB, D, XL>::kLoads, kNorm>(xs, M, K, qa.gamma, qa.eps,
                                                                      &red[0][0][0]);
   f32x4 acc[NB][MT];
   ring.run(xs, acc);
@@ -514,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void gemv_out_norm_kernel(OutNormArgs na)
   __shared__ int last;
   const GemvArgs &a = na.g;
   const int tid = threadIdx.x;
-  const int wv = tid / kWave, l = tid % kWave, g = l / 16, i16 = l % 16;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave, g = l / 16, i16 = l % 16;
   const int M = a.M, K = a.K, KP = a.KP, N = a.mat[0].N;
   const int j0 = blockIdx.x;
 
@@ -531,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void gemv_out_norm_kernel(OutNormArgs na)
   xst.load(a.x, M * K / 8);
   ring.prologue();
   bf16_t *xs = reinterpret_cast<bf16_t *>(xs4);
-  xst.template store<D * TileRing<MT, NB, D, true>::kLoads, false>(xs, ring.busy(), M, K, nullptr, 0.f,
+  xst.template store<D * TileRing<MT, NB, D, true>::kLoads, false>(xs, M, K, nullptr, 0.f,
                                                                     &red[0][0][0]);
   f32x4 acc[NB][MT];
   ring.run(xs, acc);
