@@ -332,6 +332,10 @@ def test_prefill_mfma(G, B, T, Hq, Hkv, scale):
     (3, 70, 12, 2, 12400, [4100, 12330, 9]),  # long cached prefixes next to a short one
     (7, 20, 12, 2, 200, [150, 0, 75, 180, 3, 150, 90]),  # work ranking with a tie
     (65, 5, 6, 1, 48, [(7 * i) % 44 for i in range(65)]),  # more sequences than the ranking takes
+    (2, 64, 48, 8, 4096, [0, 4032]),     # a 64-tile item next to a 1-tile one
+    (3, 33, 12, 2, 3000, [991, 1024, 2967]),  # items of 16, 17 and 47 key tiles
+    (1, 1, 16, 2, 4096, [4000]),         # one token, two head chunks, a long prefix
+    (65, 5, 6, 1, 2200, [(34 * i) % 2196 for i in range(65)]),  # long prefixes without the ranking
 ])
 def test_prefill_chunk(G, B, T, Hq, Hkv, Tmax, offsets):
     grok, U, torch = G
