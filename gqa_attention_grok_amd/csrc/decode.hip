@@ -77,7 +77,17 @@ struct DecodeArgs {
   float inv[kD / 2];      // RoPE inv_freq
 };
 
-template <bool kAppend>
+// kSpec (small grids, every workgroup resident at once): the loads are issued
+// before the sequence length is known. They cover the split's slots clamped to
+// the cache (every address stays inside [B, Tmax]); slots past the sequence
+// are masked out of the weights, and in LDS their V rows are replaced by zeros
+// (or, with the append, by the new v row) before the P.V product, so the
+// unread contents of the cache cannot reach the output. The new k / v rows
+// are loaded by every workgroup and used by the one holding the new slot.
+// This takes the length load off the path to the first K/V bytes; the
+// workgroups past the sequence load a split they do not use, so it is chosen
+// only where the grid fits the device in one go.
+template <bool kAppend, bool kSpec>
 __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[kSplit * kRowBytes];
   __shared__ float red_l[kSplitWaves][16];
@@ -108,17 +118,21 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
     g = pair % a.Hkv;
   }
   if (b >= a.B) return;
-  const int len = kAppend ? a.step[b] + 1 : a.kv_len[b];
-  if (kAppend && s == 0 && g == 0 && threadIdx.x == 0 && a.new_step)
-    a.new_step[b] = (len >= 1 && len <= a.Tmax) ? len : len - 1;
-  if (len < 1 || len > a.Tmax) return;  // reported by the combine kernel
   const int sbase = s * kSplit;
-  if (sbase >= len) return;  // whole workgroup: no barrier is skipped
+  int len = 0;
+  if constexpr (!kSpec) {
+    len = kAppend ? a.step[b] + 1 : a.kv_len[b];
+    if (kAppend && s == 0 && g == 0 && threadIdx.x == 0 && a.new_step)
+      a.new_step[b] = (len >= 1 && len <= a.Tmax) ? len : len - 1;
+    if (len < 1 || len > a.Tmax) return;  // reported by the combine kernel
+    if (sbase >= len) return;  // whole workgroup: no barrier is skipped
+  }
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lr = lane % 16, lg = lane / 16;
-  const int last = len - 1;
+  // highest slot the loads read: the sequence's last one, or (kSpec) the cache's
+  const int lim = kSpec ? a.Tmax - 1 : len - 1;
 
   // Q fragment: head row lr (zero beyond G), dims 32*kk + 8*lg; then this
   // wave's 32 K slots: the S^T A operand of key block kb is, for lane
@@ -135,6 +149,11 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   const bf16_t *vbase = a.vc + (static_cast<int64_t>(b) * a.Tmax * a.Hkv + g) * kD;
   const int64_t nrow = (static_cast<int64_t>(b) * a.Hkv + g) * kD;  // new k / v row
   const bool qok = lr < a.G;
+  // kSpec: the length is the first of the loads below (a vector load, waited
+  // for on its own by count while the others fly)
+  uint32_t lenv = 0;
+  if constexpr (kSpec)
+    asm volatile("global_load_dword %0, %1, off" : "=v"(lenv) : "v"(kAppend ? a.step + b : a.kv_len + b) : "memory");
   u32x4 qw[4], kf[2][4];
   {
     const bf16_t *qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (qok ? lr : 0)) * kD;
@@ -144,23 +163,43 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   bool knew[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int kj = min(sbase + 32 * wave + k_row_key(16 * kb + lr), last);
-    knew[kb] = kAppend && kj == last;
+    const int kj = min(sbase + 32 * wave + k_row_key(16 * kb + lr), lim);
+    knew[kb] = kAppend && !kSpec && kj == lim;
     const bf16_t *kp = (knew[kb] ? a.kn + nrow : kbase + kj * rstride) + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kf[kb][kk]) : "v"(kp + 32 * kk) : "memory");
+  }
+  // kSpec + append: the new k row (this lane's dims of it) and chunk lane % 16
+  // of the new v row, for the workgroup that holds the new slot
+  u32x4 nk[kAppend && kSpec ? 4 : 1], nv;
+  if constexpr (kAppend && kSpec) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(nk[kk]) : "v"(a.kn + nrow + 32 * kk + 8 * lg) : "memory");
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(nv) : "v"(a.vn + nrow + 8 * (lane % 16)) : "memory");
   }
   {
     const int lrow = lane / 16, lchunk = lane % 16;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int R = 32 * wave + 4 * j + lrow;
-      const int vj = min(sbase + R, last);
-      const bf16_t *vrow = (kAppend && vj == last) ? a.vn + nrow : vbase + vj * rstride;
+      const int vj = min(sbase + R, lim);
+      const bf16_t *vrow = (kAppend && !kSpec && vj == lim) ? a.vn + nrow : vbase + vj * rstride;
       __builtin_amdgcn_global_load_lds(vrow + 8 * (lchunk ^ v_swz(R)),
                                        (lds_void *)(&Vs[(32 * wave + 4 * j) * kRowBytes]), 16, 0, 0);
     }
   }
+  if constexpr (kSpec) {
+    // loads issued after the length: q 4, K 8, new k / v rows 5 (append), V 8
+    if constexpr (kAppend)
+      asm volatile("s_waitcnt vmcnt(25)" : "+v"(lenv) : : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(20)" : "+v"(lenv) : : "memory");
+    len = __builtin_amdgcn_readfirstlane(static_cast<int>(lenv)) + (kAppend ? 1 : 0);
+    if (kAppend && s == 0 && g == 0 && threadIdx.x == 0 && a.new_step)
+      a.new_step[b] = (len >= 1 && len <= a.Tmax) ? len : len - 1;
+  }
+  const int last = len - 1;
   if constexpr (kAppend) {
     // cos/sin of the new position, once per workgroup, while the loads fly
     // (the table is read with uniform indices: scalar loads, which do not
@@ -180,6 +219,24 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
                  "+v"(kf[0][3]), "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(kf[1][2]), "+v"(kf[1][3])
                :
                : "memory");
+  if constexpr (kSpec) {
+    if constexpr (kAppend)  // landed with the wait above (issued before the V loads)
+      asm volatile("" : "+v"(nk[0]), "+v"(nk[1]), "+v"(nk[2]), "+v"(nk[3]), "+v"(nv));
+    if (len < 1 || len > a.Tmax || sbase >= len) {  // whole workgroup
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the V loads write this workgroup's LDS
+      return;
+    }
+    if constexpr (kAppend) {
+      // slots at or past the new one take the new k row (as the clamped rows
+      // of the other form do)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        knew[kb] = sbase + 32 * wave + k_row_key(16 * kb + lr) >= last;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[kb][kk] = knew[kb] ? nk[kk] : kf[kb][kk];
+      }
+    }
+  }
   if constexpr (kAppend) {
     // lane (lr, lg) holds dims 32*kk + 8*lg + e of its rows: kk = 0, 1 pair
     // with kk = 2, 3 (dim + 64)
@@ -245,6 +302,20 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 3) void decode_split_kernel(De
   u32x4 pw2 = pw;
   asm volatile("s_waitcnt vmcnt(0)" : "+v"(pw2), "+v"(lsum) : : "memory");
   const bf16x8 pf = __builtin_bit_cast(bf16x8, pw2);
+  if constexpr (kSpec) {
+    // this wave's V rows past the sequence: zeros, or the new v row from the
+    // new slot on (what the clamped loads of the other form put there)
+    const int first = kAppend ? last : last + 1;
+    if (sbase + 32 * wave + 31 >= first) {  // wave-uniform
+      const u32x4 fill = kAppend ? nv : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int R = 32 * wave + 4 * j + lane / 16;
+        if (sbase + R >= first)
+          *reinterpret_cast<u32x4 *>(&Vs[R * kRowBytes + 16 * ((lane % 16) ^ v_swz(R))]) = fill;
+      }
+    }
+  }
   if constexpr (kAppend) {
     // the new v row landed in LDS row last - sbase of this wave: copy it to
     // its cache slot (16 lanes x 16 bytes, undoing the chunk swizzle)
@@ -309,11 +380,31 @@ constexpr int kSplitGroups = kCombineThreads / (kD / 4);  // 8 groups of 32 floa
 
 // One workgroup per (sequence, query head): 32 lanes x float4 cover the head's
 // 128 outputs; 8 groups take every 8th split; the groups are added in LDS.
+// kSpec: the first round of partial loads goes out before the length is known
+// (splits past the sequence hold stale values and are not added).
+template <bool kSpec>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
   __shared__ f32x4 red_o[kSplitGroups][kD / 4];
   __shared__ float red_l[kSplitGroups];
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int g = h / a.G, hh = h % a.G;
+  const int c = threadIdx.x % (kD / 4), sg = threadIdx.x / (kD / 4);
+  const int64_t base = (static_cast<int64_t>(b) * a.Hkv + g) * a.S;
+  // Up to 8 partials per thread per round, all loads issued before any sum, so
+  // a round costs one memory latency (one round covers 64 splits = 8192 slots).
+  constexpr int kU = 8;
+  f32x4 vo[kU];
+  float vl[kU];
+  auto load_round = [&](int sp0, int ns) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int sp = sp0 + u * kSplitGroups;
+      const int64_t row = (base + (sp < ns ? sp : 0)) * a.G + hh;
+      vo[u] = *reinterpret_cast<const f32x4 *>(a.part_o + row * kD + 4 * c);
+      vl[u] = a.part_l[row];
+    }
+  };
+  if constexpr (kSpec) load_round(sg, a.S);
   const int len = a.step ? a.step[b] + 1 : a.kv_len[b];
   bf16_t *orow = a.out + (static_cast<int64_t>(b) * a.Hq + h) * kD;
   if (len < 1 || len > a.Tmax) {  // outside the contract: zero row, flag it
@@ -322,11 +413,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     return;
   }
   const int ns = (len + a.split_keys - 1) / a.split_keys;
-  const int c = threadIdx.x % (kD / 4), sg = threadIdx.x / (kD / 4);
-  const int64_t base = (static_cast<int64_t>(b) * a.Hkv + g) * a.S;
-  // Up to 8 partials per thread per round, all loads issued before any sum, so
-  // a round costs one memory latency (one round covers 64 splits = 8192 slots).
-  constexpr int kU = 8;
   f32x4 acc[4];
   float l[4];
 #pragma unroll
@@ -335,15 +421,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     l[u] = 0.f;
   }
   for (int sp0 = sg; sp0 < ns; sp0 += kU * kSplitGroups) {
-    f32x4 vo[kU];
-    float vl[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int sp = sp0 + u * kSplitGroups;
-      const int64_t row = (base + (sp < ns ? sp : 0)) * a.G + hh;
-      vo[u] = *reinterpret_cast<const f32x4 *>(a.part_o + row * kD + 4 * c);
-      vl[u] = a.part_l[row];
-    }
+    if (!kSpec || sp0 != sg) load_round(sp0, ns);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (sp0 + u * kSplitGroups < ns) {
@@ -400,6 +478,31 @@ int64_t split_blocks(const DecodeArgs &a) {
   const int64_t n = kXcds * ((pairs + kXcds - 1) / kXcds) * a.S;
   return n > 0x7fffffff ? 0 : n;
 }
+
+// Grids up to this many split workgroups are resident at once (256 CUs, three
+// workgroups each by the kernel's launch bounds): they take the speculative
+// loads.
+constexpr int64_t kSpecMaxBlocks = 256 * 3;
+
+template <bool kAppend>
+hipError_t launch_split_combine(const DecodeArgs &a, hipStream_t st) {
+  const int64_t nblk = split_blocks(a);
+  if (nblk == 0) return hipErrorInvalidConfiguration;
+  const bool spec = nblk <= kSpecMaxBlocks;
+  const dim3 grid(static_cast<unsigned>(nblk)), block(kSplitWaves * kWave);
+  if (spec)
+    hipLaunchKernelGGL((decode_split_kernel<kAppend, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<kAppend, false>), grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cgrid(static_cast<unsigned>(a.B * a.Hq));
+  if (spec)
+    hipLaunchKernelGGL(decode_combine_kernel<true>, cgrid, dim3(kCombineThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<false>, cgrid, dim3(kCombineThreads), 0, st, a);
+  return hipGetLastError();
+}
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int Tmax, int Hq, int Hkv) {
@@ -437,14 +540,7 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
   a.step = nullptr;
   a.new_step = nullptr;
   a.q_out = nullptr;
-  const int64_t nblk = split_blocks(a);
-  if (nblk == 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_split_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(kSplitWaves * kWave), 0, st,
-                     a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_split_combine<false>(a, st);
 }
 
 hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, void *kc, void *vc,
@@ -479,14 +575,7 @@ hipError_t launch_decode_append(const void *q, const void *kn, const void *vn, v
   a.new_step = new_step;
   a.q_out = static_cast<bf16_t *>(q_out);
   for (int i = 0; i < kD / 2; ++i) a.inv[i] = f.inv[i];
-  const int64_t nblk = split_blocks(a);
-  if (nblk == 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_split_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(kSplitWaves * kWave), 0, st,
-                     a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombineThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_split_combine<true>(a, st);
 }
 
 }  // namespace grok

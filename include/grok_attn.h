@@ -309,7 +309,11 @@ GROK_API int grok_attn_prefill_rope(const void *q, const void *k, const void *v,
  * j < kv_len[b]):
  *   out[b, 0, h*D:(h+1)*D] = sum_{j < kv_len[b]} softmax_j(softcap(attn_mult *
  *                             <q[b,0,h], k_cache[b,j,g]>)) * v_cache[b,j,g]
- * Slots j >= kv_len[b] are never read.
+ * Slots j >= kv_len[b] never affect the output, whatever they hold (NaN and
+ * Inf included). When the grid is small enough to be resident at once (at
+ * most 768 workgroups: B*Hkv rounded up to a multiple of 8, times
+ * ceil(Tmax/128)), the kernel may read them: it loads each 128-slot block
+ * before its sequence's length arrives and discards what lies past it.
  *   q [B, 1, Hq, D]; caches [B, Tmax, Hkv, D]; kv_len [B] int32 device
  *   (= step + 1 after the new token was appended); out [B, 1, Hq*D]; bf16.
  *   workspace: device scratch of at least grok_attn_decode_workspace_bytes()

@@ -525,6 +525,91 @@ def test_decode_append_matches_unfused_calls(G, Hq, Hkv, lens, Tmax):
     np.testing.assert_array_equal(res[1][4], lens)
 
 
+def _poison_past(cache, lens):
+    """NaN and Inf bit patterns in every cache slot at or past lens[b]."""
+    c = cache.copy()
+    for b, n in enumerate(lens):
+        tail = c[b, n:]
+        tail[...] = 0x7FC0                        # NaN
+        tail[::2, ..., ::3] = 0x7F80              # +Inf
+        tail[1::2, ..., 1::3] = 0xFF80            # -Inf
+    return c
+
+
+# 2 sequences: 16 (sequence, KV head) pairs x 8 splits, a grid resident at once
+# (loads issued before the lengths arrive); 13 sequences: 832 workgroups, the
+# lengths read first
+@pytest.mark.parametrize("B", [2, 13])
+def test_decode_reads_nothing_past_the_length(G, B):
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    Hq, Hkv, D, Tmax = 48, 8, 128, 1024
+    lens = [(397 * b + 129) % Tmax + 1 for b in range(B)]
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=41 + B, lengths=lens)
+    mult = 1 / math.sqrt(D)
+    kv_len = np.asarray(lens, np.int32)
+    # decode against poisoned tails = decode against the clean cache, bit for bit
+    outs = []
+    for kcache, vcache in ((p["k_cache"], p["v_cache"]),
+                           (_poison_past(p["k_cache"], lens), _poison_past(p["v_cache"], lens))):
+        out = torch.empty((B, 1, Hq * D), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(grok.grok_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, D), dtype=torch.uint8,
+                         device="cuda")
+        grok.grok_attn_decode(U.dev_bf16(p["q"]), U.dev_bf16(kcache), U.dev_bf16(vcache), U.dev(kv_len), out, ws,
+                              mult)
+        outs.append(U.bits(out))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    mask = orc.attention_mask((kv_len - 1)[:, None], Tmax, kv_len=kv_len)
+    ref = orc.attention(orc.bf16_bits_to_f64(p["q"]), orc.bf16_bits_to_f64(p["k_cache"]),
+                        orc.bf16_bits_to_f64(p["v_cache"]), mask, mult, 30.0)
+    U.assert_bf16_close(orc.bf16_bits_to_f64(outs[1]), ref, "decode, poisoned tails")
+    # the fused step: slots past the new one poisoned
+    res = []
+    for poison in (False, True):
+        kc0 = _poison_past(p["k_cache"], lens) if poison else p["k_cache"]
+        vc0 = _poison_past(p["v_cache"], lens) if poison else p["v_cache"]
+        kc, vc = U.dev_bf16(kc0), U.dev_bf16(vc0)
+        st = pipe.DecodeStep(kc, vc, U.dev_bf16(p["q"]), U.dev_bf16(p["k_new"]), U.dev_bf16(p["v_new"]),
+                             U.dev(p["step"]), mult)
+        out = st()
+        torch.cuda.synchronize()
+        assert st.status.item() == 0
+        res.append(U.bits(out))
+    np.testing.assert_array_equal(res[0], res[1])
+
+
+def test_decode_grid_forms_agree(G):
+    """A sequence decoded alone (a grid resident at once, loads issued before
+    its length arrives) and within a batch of 13 (lengths read first) gives
+    the same bits, plain and with the append."""
+    grok, U, torch = G
+    import gqa_attention_grok_amd.pipeline as pipe
+    B, Hq, Hkv, D, Tmax = 13, 48, 8, 128, 1024
+    lens = [(233 * b + 77) % Tmax + 1 for b in range(B)]
+    p = gi.make_decode_inputs(B, Hq, Hkv, D, Tmax, seed=43, lengths=lens)
+    mult = 1 / math.sqrt(D)
+
+    def run(sl):
+        n = sl.stop - sl.start
+        kl = np.asarray(lens[sl], np.int32)
+        out = torch.empty((n, 1, Hq * D), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(grok.grok_attn_decode_workspace_bytes(n, Tmax, Hq, Hkv, D), dtype=torch.uint8,
+                         device="cuda")
+        grok.grok_attn_decode(U.dev_bf16(p["q"][sl]), U.dev_bf16(p["k_cache"][sl]), U.dev_bf16(p["v_cache"][sl]),
+                              U.dev(kl), out, ws, mult)
+        st = pipe.DecodeStep(U.dev_bf16(p["k_cache"][sl]), U.dev_bf16(p["v_cache"][sl]), U.dev_bf16(p["q"][sl]),
+                             U.dev_bf16(p["k_new"][sl]), U.dev_bf16(p["v_new"][sl]), U.dev(p["step"][sl]), mult)
+        fused = st()
+        torch.cuda.synchronize()
+        return U.bits(out), U.bits(fused), U.bits(st.k_cache), U.bits(st.v_cache)
+
+    whole = run(slice(0, B))
+    for b in (0, 5, 12):
+        alone = run(slice(b, b + 1))
+        for x, y in zip(whole, alone):
+            np.testing.assert_array_equal(x[b:b + 1], y)
+
+
 def test_decode_append_bad_step(G):
     grok, U, torch = G
     import gqa_attention_grok_amd.pipeline as pipe
