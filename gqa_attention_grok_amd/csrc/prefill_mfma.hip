@@ -87,15 +87,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
   const int lr = lane % 16;  // this lane's row inside a row block
   const int lg = lane / 16;  // this lane's k/key group
 
-  // blockIdx -> (g, head chunk, query tile (longest first), batch); g fastest so
-  // that, with 8 KV heads, all tiles of one KV head land on one XCD's L2.
+  // blockIdx -> (g, head chunk, sequence, query tile); g fastest so that, with
+  // 8 KV heads, all tiles of one KV head land on one XCD's L2; the query tile
+  // slowest, longest first, so that the causally longest tiles of every
+  // sequence start before any shorter one (the grid runs in several rounds of
+  // resident workgroups, and the shortest tiles fill the last round).
   int id = blockIdx.x;
   const int g = id % a.Hkv;
   id /= a.Hkv;
   const int hc = id % a.nhc;
   id /= a.nhc;
-  int qt = a.nqt - 1 - (id % a.nqt);
-  int b = id / a.nqt;
+  int qt = a.nqt - 1 - id / a.B;
+  int b = id % a.B;
   if constexpr (kOffset) {
     // Chunks after cached prefixes of different lengths: the work of a query
     // tile grows with its sequence's offset. Items (sequence, query tile) are
