@@ -87,6 +87,21 @@ __device__ __forceinline__ void read_vt_half(u32x2 *lo, u32x2 *hi, const uint32_
    ...);
 }
 
+// 16-byte LDS read as inline assembly (same reason as above); its result is
+// used only after lds_wait4.
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// Waits until at most kLeft LDS operations are outstanding, with four 16-byte
+// fragments passing through.
+template <int kLeft>
+__device__ __forceinline__ void lds_wait4(u32x4 *r) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "i"(kLeft));
+}
+
 // Waits until at most kLeft LDS operations are outstanding; the four fragment
 // pairs pass through so that no use of them is scheduled above the wait.
 template <int kLeft>

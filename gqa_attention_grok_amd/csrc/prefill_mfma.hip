@@ -301,15 +301,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       f32x4 sacc[kRB][2];
 #pragma unroll
       for (int i = 0; i < kRB; ++i) sacc[i][0] = sacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kOffset) {
+        // K fragments as inline-assembly LDS reads: in this instantiation the
+        // compiler otherwise waits for the next tile's loads (all of them)
+        // before the first read, which serialises the prefetch with the tile.
+        // Both key blocks' reads go out, then each is waited for by count.
+        u32x4 kr[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int R = 32 * h + 16 * kb + lr;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ks[buf][k_byte(R, 4 * kk + lg)]);
+          for (int kk = 0; kk < 4; ++kk)
+            kr[kb][kk] = lds_read_b128(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                (lds_void *)(&Ks[buf][k_byte(32 * h + 16 * kb + lr, 4 * kk + lg)]))));
+        lds_wait4<4>(kr[0]);
 #pragma unroll
-          for (int i = 0; i < kRB; ++i)
-            sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[i][kk], sacc[i][kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb == 1) lds_wait4<0>(kr[1]);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < kRB; ++i)
+              sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kb][kk]),
+                                                                   qf[i][kk], sacc[i][kb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int R = 32 * h + 16 * kb + lr;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ks[buf][k_byte(R, 4 * kk + lg)]);
+#pragma unroll
+            for (int i = 0; i < kRB; ++i)
+              sacc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[i][kk], sacc[i][kb], 0, 0, 0);
+          }
         }
       }
       // softcap + shifted exp -> P (bf16) in the B-operand layout of P.V:
