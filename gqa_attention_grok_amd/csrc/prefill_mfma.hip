@@ -79,7 +79,7 @@ template <bool kHasValid, bool kOffset, bool kRopeQ = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][kTileBytes];
-  __shared__ uint8_t kvs[2][kBN];
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kBN];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -207,9 +207,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     }
   };
   uint8_t kvr = 0;
+  // the sequence's key-valid row (wave-uniform base; the lane offset is 32-bit)
+  const uint8_t *kvrow = kHasValid ? a.key_valid + static_cast<int64_t>(b) * a.T : nullptr;
   auto load_valid = [&](int key0) {
     if constexpr (kHasValid) {
-      if (tid < kBN) kvr = (key0 + tid < a.T) ? a.key_valid[static_cast<int64_t>(b) * a.T + key0 + tid] : 0;
+      const int j = key0 + tid;
+      if (tid < kBN) kvr = j < a.T ? kvrow[j] : 0;
     }
   };
   auto store_valid = [&](int buf) {
@@ -285,8 +288,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
     const int key0 = t * kBN;
     const bool more = !kMask || t + 1 < ntiles;  // unmasked tiles always have a successor
     if (more) {
-      issue_tile(key0 + kBN, buf ^ 1);
+      // (the key-valid byte first: whatever the compiler waits for to issue
+      // it is then not behind the tile loads)
       load_valid(key0 + kBN);
+      issue_tile(key0 + kBN, buf ^ 1);
     }
     uint32_t amb[8];
 #pragma unroll
@@ -301,11 +306,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
       f32x4 sacc[kRB][2];
 #pragma unroll
       for (int i = 0; i < kRB; ++i) sacc[i][0] = sacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kOffset) {
-        // K fragments as inline-assembly LDS reads: in this instantiation the
-        // compiler otherwise waits for the next tile's loads (all of them)
-        // before the first read, which serialises the prefetch with the tile.
-        // Both key blocks' reads go out, then each is waited for by count.
+      u32x2 kv8 = {0u, 0u};  // kHasValid: this lane's 8 key-valid bytes of the half
+      if constexpr (kOffset || kHasValid) {
+        // K fragments (and the key-valid bytes) as inline-assembly LDS reads:
+        // in these instantiations the compiler otherwise waits for the next
+        // tile's loads (all of them) before the first read, which serialises
+        // the prefetch with the tile. The reads go out, then each key block
+        // is waited for by count.
+        if constexpr (kHasValid)
+          asm volatile("ds_read_b64 %0, %1" : "=v"(kv8)
+                       : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)(&kvs[buf][32 * h + 8 * lg]))))
+                       : "memory");
         u32x4 kr[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -314,6 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
             kr[kb][kk] = lds_read_b128(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                 (lds_void *)(&Ks[buf][k_byte(32 * h + 16 * kb + lr, 4 * kk + lg)]))));
         lds_wait4<4>(kr[0]);
+        if constexpr (kHasValid) asm volatile("" : "+v"(kv8));  // issued before kr[0]: landed
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb == 1) lds_wait4<0>(kr[1]);
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(PrefillArgs a
           for (int e = 0; e < 8; ++e) {
             const int key = hk0 + 8 * lg + e;
             bool ok = key <= pos[i];
-            if constexpr (kHasValid) ok = ok && kvs[buf][32 * h + 8 * lg + e] != 0;
+            if constexpr (kHasValid) ok = ok && ((kv8[e >> 2] >> (8 * (e & 3))) & 0xffu) != 0;
             p[e] = ok ? p[e] : 0.f;
           }
         }
