@@ -120,6 +120,33 @@ def test_prefill_b1_t8192_sampled(G):
     print(f"prefill sampled {len(rows)} rows x {Hq} heads, max abs err {max(errs):.2e}")
 
 
+def test_prefill_padded_b2_t4096_sampled(G):
+    """Long prompts with key padding (10 % of the keys, and the whole first 64
+    keys of sequence 1): sampled rows of every head against the oracle, the
+    first rows of sequence 1 having no valid key at all (equal weights over
+    all T value rows)."""
+    grok, pipe, U, torch = G
+    B, T, Hq, Hkv, D = 2, 4096, 48, 8, 128
+    mult = 1 / np.sqrt(D)
+    p = gi.make_prefill_inputs(B, T, Hq, Hkv, D, seed=2024, key_pad_frac=0.1)
+    kv = p["key_valid"].copy()
+    kv[1, :64] = 0
+    out = torch.empty((B, T, Hq * D), dtype=torch.bfloat16, device="cuda")
+    grok.grok_attn_prefill(U.dev_bf16(p["q"]), U.dev_bf16(p["k"]), U.dev_bf16(p["v"]), out, mult,
+                           key_valid=U.dev(kv))
+    torch.cuda.synchronize()
+    q, k, v = (orc.bf16_bits_to_f64(p[n]) for n in ("q", "k", "v"))
+    g = gi.rng(4242)
+    rows = [0, 1, 63, 64, 65, 2047, 4094, 4095] + list(g.integers(0, T, 8))
+    for b in range(B):
+        got = U.host(out[b, rows]).reshape(len(rows), Hq, D)
+        for r, t in enumerate(rows):
+            mask_row = (np.arange(T) <= t) & (kv[b] != 0)
+            for h in range(Hq):
+                ref = orc.attention_rows(q, k, v, b, t, h, mask_row, mult)
+                U.assert_bf16_close(got[r, h], ref, f"padded prefill b={b} t={t} h={h}")
+
+
 def test_prefill_b1_t8192_two_heads_every_row(G):
     """Every one of the 8192 query rows of two heads in different KV groups
     (head 0 on KV head 0, head 47 on KV head 7) against the oracle: all 256
