@@ -1,9 +1,10 @@
 """GPU parity against the fp64 oracle on seeded random shapes: prefill (bf16
 MFMA path, optional key padding; fp32 generic path), decode (plain and with the
 append fused), chunked prefill after cached prefixes, RMSNorm and the int8
-Linears (tiled and few-row). The shapes are drawn
-once from a fixed seed, so every run checks the same cases; each case prints
-its shape in the test id."""
+Linears (tiled and few-row), with a few longer cases (prompts up to 1200 rows,
+decode batches of 6-20 sequences, prefixes of 1000-4000 slots). The shapes are
+drawn once from fixed seeds, so every run checks the same cases; each case
+prints its shape in the test id."""
 import math
 
 import numpy as np
@@ -55,6 +56,26 @@ def _chunk_cases(n):
 PREFILL = _prefill_cases(8)
 DECODE = _decode_cases(6)
 CHUNK = _chunk_cases(6)
+
+# Longer cases from a stream of their own (the cases above keep their draws):
+# prompts up to 1200 rows, batches of decode that cross from grids resident
+# at once to larger ones, chunks after prefixes of 1000-4000 slots.
+_rng3 = np.random.default_rng(20261204)
+for _ in range(3):
+    hq, hkv = (lambda h: (h * int(_rng3.choice([1, 2, 3, 6])), h))(int(_rng3.choice([1, 2, 4, 8])))
+    PREFILL.append((int(_rng3.integers(1, 3)), int(_rng3.integers(300, 1201)), hq, hkv,
+                    float(_rng3.choice([1.0, 4.0])), bool(_rng3.integers(0, 2)), int(_rng3.integers(0, 1 << 30))))
+for _ in range(3):
+    hq, hkv = (lambda h: (h * int(_rng3.choice([1, 2, 3, 6])), h))(int(_rng3.choice([1, 2, 4, 8])))
+    B, Tmax = int(_rng3.integers(6, 21)), int(_rng3.integers(500, 3001))
+    DECODE.append((hq, hkv, Tmax, [int(x) for x in _rng3.integers(1, Tmax + 1, size=B)],
+                   int(_rng3.integers(0, 1 << 30))))
+for _ in range(3):
+    hq, hkv = (lambda h: (h * int(_rng3.choice([1, 2, 3, 6])), h))(int(_rng3.choice([1, 2, 4, 8])))
+    B, T = int(_rng3.integers(1, 4)), int(_rng3.integers(1, 301))
+    Tmax = T + int(_rng3.integers(1000, 4001))
+    CHUNK.append((hq, hkv, T, Tmax, [int(x) for x in _rng3.integers(0, Tmax - T + 1, size=B)],
+                  int(_rng3.integers(0, 1 << 30))))
 
 
 @pytest.fixture(scope="module")
